@@ -1,0 +1,171 @@
+"""ctypes binding over libfmha_mqa.so (argument marshalling only).
+
+PyTorch supplies device memory (``tensor.data_ptr()``) and the stream
+(``torch.cuda.current_stream().cuda_stream``); every step of the attention
+runs in the library's HIP kernels.  Importing this module fails loudly when the
+library has not been built: there is no fallback path of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfmha_mqa.so")
+
+FMHA_F32 = 0
+FMHA_BF16 = 1
+
+# Every symbol include/fmha_mqa.h declares, with its ctypes signature.
+_c_int, _c_size, _c_void_p, _c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+SIGNATURES = {
+    "fmha_mqa_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "fmha_mqa_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                              _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                              _c_int, _c_int, _c_void_p, _c_size, _c_void_p]),
+    "fmha_lse_merge": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
+                                _c_int, _c_void_p, _c_void_p]),
+    "fmha_status_string": (ctypes.c_char_p, [_c_int]),
+}
+
+
+class FmhaError(RuntimeError):
+    """A non-zero fmha_status from the library."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first with `python -m fmha_mqa_fwd_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def status_string(status: int) -> str:
+    return _lib.fmha_status_string(int(status)).decode()
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return FMHA_F32
+    if dt == torch.bfloat16:
+        return FMHA_BF16
+    raise ValueError(f"out dtype must be float32 or bfloat16, got {dt}")
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def default_scale(hd: int) -> float:
+    """1/sqrt(hd) as the fp32 value the kernel receives."""
+    return float(torch.tensor(1.0 / math.sqrt(hd), dtype=torch.float32))
+
+
+def workspace_bytes(B: int, T: int, n_h: int, hd: int, num_splits: int) -> int:
+    return int(_lib.fmha_mqa_workspace_bytes(B, T, n_h, hd, num_splits))
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+        kv_idx: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+        out_dtype: torch.dtype = torch.bfloat16, num_splits: int = 1,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None, stream=None
+        ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Multi-query attention forward (see include/fmha_mqa.h).
+
+    q [B, T, n_h, hd] bf16; dense k, v [B, s_k, hd] bf16, or pools [P, hd] with
+    kv_idx [B, T, s_k] int32.  Returns (out [B, T, n_h, hd], lse [B, T, n_h] fp32).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, n_h, hd]")
+    B, T, n_h, hd = q.shape
+    if kv_idx is None:
+        if k.dim() != 3 or k.shape[0] != B or k.shape[2] != hd or v.shape != k.shape:
+            raise ValueError("dense k/v must be [B, s_k, hd] with q's B and hd")
+        s_k, pool_rows = k.shape[1], 0
+    else:
+        if k.dim() != 2 or k.shape[1] != hd or v.shape != k.shape:
+            raise ValueError("gather k/v pools must be [P, hd] with q's hd")
+        if kv_idx.dtype != torch.int32 or tuple(kv_idx.shape[:2]) != (B, T) or kv_idx.dim() != 3:
+            raise ValueError("kv_idx must be int32 [B, T, s_k]")
+        s_k, pool_rows = kv_idx.shape[2], k.shape[0]
+        if not kv_idx.is_contiguous():
+            raise ValueError("kv_idx must be contiguous")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    dev = q.device
+    if scale is None:
+        scale = default_scale(hd)
+    if out is None:
+        out = torch.empty((B, T, n_h, hd), dtype=out_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, T, n_h), dtype=torch.float32, device=dev)
+    ws_need = workspace_bytes(B, T, n_h, hd, num_splits)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.fmha_mqa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(out), _ptr(lse),
+                           B, T, n_h, s_k, hd, pool_rows, float(scale),
+                           _dtype_code(out.dtype), int(num_splits), _ptr(workspace), ws_bytes,
+                           _stream_handle(stream))
+    if st != 0:
+        raise FmhaError("fmha_mqa_fwd", st)
+    return out, lse
+
+
+def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
+              out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None, stream=None
+              ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Merge fp32 partials o_parts [P, R, hd] / lse_parts [P, R] (natural log)."""
+    if o_parts.dim() != 3 or lse_parts.shape != o_parts.shape[:2]:
+        raise ValueError("o_parts must be [P, R, hd] and lse_parts [P, R]")
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("partials must be contiguous")
+    P, R, hd = o_parts.shape
+    dev = o_parts.device
+    if out is None:
+        out = torch.empty((R, hd), dtype=out_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((R,), dtype=torch.float32, device=dev)
+    st = _lib.fmha_lse_merge(_ptr(o_parts), _ptr(lse_parts), P, R, hd, _ptr(out),
+                             _dtype_code(out.dtype), _ptr(lse), _stream_handle(stream))
+    if st != 0:
+        raise FmhaError("fmha_lse_merge", st)
+    return out, lse
+
+
+def raw_fwd(*args) -> int:
+    """The C entry point itself, for tests of argument validation."""
+    return int(_lib.fmha_mqa_fwd(*args))
+
+
+def raw_merge(*args) -> int:
+    return int(_lib.fmha_lse_merge(*args))

@@ -1,0 +1,143 @@
+// C ABI of libfmha_mqa.so: argument validation, work decomposition and
+// launches.  Declarations and the contract live in include/fmha_mqa.h.
+//
+// Every function validates all arguments before it enqueues anything, never
+// allocates, frees or synchronises, and reports errors as status codes.  The
+// compile-once / launch-many shape and the absence of host syncs follow the
+// lessons in the dsv4/kernels/cuda commit log (per-call JIT and .item() syncs
+// dominated the time there).
+#include <math.h>
+#include <stdint.h>
+
+#include "fmha_internal.h"
+#include "fmha_mqa.h"
+
+namespace {
+
+constexpr size_t kRegionAlign = 256;
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// Workspace layout for split-KV: o_part fp32 [S, rows, hd], then lse_part fp32 [S, rows].
+struct WsLayout {
+  size_t o_bytes, lse_off, total;
+};
+
+inline WsLayout ws_layout(int64_t rows, int hd, int splits) {
+  WsLayout w;
+  w.o_bytes = round_up((size_t)splits * (size_t)rows * (size_t)hd * 4u, kRegionAlign);
+  w.lse_off = w.o_bytes;
+  w.total = w.o_bytes + round_up((size_t)splits * (size_t)rows * 4u, kRegionAlign);
+  return w;
+}
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+size_t fmha_mqa_workspace_bytes(int B, int T, int n_h, int hd, int num_splits) {
+  if (B < 0 || T < 0 || n_h < 0 || hd <= 0 || num_splits < 1) return 0;
+  if (num_splits == 1) return 0;
+  const int64_t rows = (int64_t)B * T * n_h;
+  return ws_layout(rows, hd, num_splits).total;
+}
+
+int fmha_mqa_fwd(const void* q, const void* k, const void* v, const int32_t* kv_idx, void* out,
+                 float* lse, int B, int T, int n_h, int s_k, int hd, int pool_rows, float scale,
+                 int out_dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (out_dtype != FMHA_F32 && out_dtype != FMHA_BF16) return FMHA_ERR_INVALID_ARG;
+  if (B < 0 || T < 0 || n_h < 0 || s_k < 0 || num_splits < 1) return FMHA_ERR_INVALID_ARG;
+  if (hd != 64 && hd != 128 && hd != 256) return FMHA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale)) return FMHA_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)B * T * n_h;
+  if (rows == 0) return FMHA_OK;  // nothing to compute
+  if (rows > INT32_MAX) return FMHA_ERR_UNSUPPORTED;
+  if (num_splits > (s_k > 1 ? s_k : 1)) return FMHA_ERR_INVALID_ARG;
+  if (!q || !out || !lse) return FMHA_ERR_INVALID_ARG;
+  const bool gather = kv_idx != nullptr;
+  if (s_k > 0) {
+    if (!k || !v) return FMHA_ERR_INVALID_ARG;
+    if (gather && pool_rows < 1) return FMHA_ERR_INVALID_ARG;
+    if ((int64_t)B * T * s_k > INT64_MAX / 4) return FMHA_ERR_UNSUPPORTED;
+  }
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4)) return FMHA_ERR_ALIGNMENT;
+  if (s_k > 0 && (!aligned(k, 16) || !aligned(v, 16))) return FMHA_ERR_ALIGNMENT;
+  if (gather && !aligned(kv_idx, 4)) return FMHA_ERR_ALIGNMENT;
+
+  fmha::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.kv_idx = (gather && s_k > 0) ? kv_idx : nullptr;
+  p.total_rows = rows;
+  p.rows_per_group = gather ? n_h : T * n_h;
+  p.n_groups = gather ? B * T : B;
+  p.s_k = s_k;
+  p.pool_rows = gather ? pool_rows : 0;
+  p.num_splits = num_splits;
+  p.chunk = (s_k + num_splits - 1) / num_splits;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  if (gather && s_k == 0) p.n_groups = B * T;  // still one group per token
+
+  const int64_t grid = fmha::fwd_grid_size(p, hd);
+  if (grid > INT32_MAX) return FMHA_ERR_UNSUPPORTED;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // launch errors below are ours alone
+
+  if (num_splits == 1) {
+    p.out = out;
+    p.lse = lse;
+    p.out_mode = out_dtype == FMHA_BF16 ? fmha::OUT_BF16 : fmha::OUT_F32;
+    return launch_status(fmha::launch_fwd(p, hd, st));
+  }
+
+  const WsLayout wl = ws_layout(rows, hd, num_splits);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < wl.total)
+    return FMHA_ERR_WORKSPACE;
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.lse_off);
+  p.out = o_part;
+  p.lse = lse_part;
+  p.out_mode = fmha::OUT_PARTIAL;
+  int s = launch_status(fmha::launch_fwd(p, hd, st));
+  if (s != FMHA_OK) return s;
+  return launch_status(fmha::launch_merge(o_part, lse_part, num_splits, (int)rows, hd, out,
+                                          out_dtype == FMHA_BF16, lse, st));
+}
+
+int fmha_lse_merge(const float* o_parts, const float* lse_parts, int n_parts, int rows, int hd,
+                   void* out, int out_dtype, float* lse, void* stream) {
+  if (out_dtype != FMHA_F32 && out_dtype != FMHA_BF16) return FMHA_ERR_INVALID_ARG;
+  if (n_parts < 1 || rows < 0 || hd < 4 || (hd % 4) != 0) return FMHA_ERR_INVALID_ARG;
+  if (rows == 0) return FMHA_OK;
+  if (!o_parts || !lse_parts || !out) return FMHA_ERR_INVALID_ARG;
+  if ((int64_t)n_parts * rows * hd > (INT64_MAX / 8)) return FMHA_ERR_UNSUPPORTED;
+  if (!aligned(o_parts, 16) || !aligned(lse_parts, 4)) return FMHA_ERR_ALIGNMENT;
+  if (!aligned(out, out_dtype == FMHA_BF16 ? 8 : 16)) return FMHA_ERR_ALIGNMENT;
+  if (lse && !aligned(lse, 4)) return FMHA_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return launch_status(fmha::launch_merge(o_parts, lse_parts, n_parts, rows, hd, out,
+                                          out_dtype == FMHA_BF16, lse,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+const char* fmha_status_string(int status) {
+  switch (status) {
+    case FMHA_OK: return "ok";
+    case FMHA_ERR_INVALID_ARG: return "invalid argument";
+    case FMHA_ERR_UNSUPPORTED: return "unsupported head dim or size";
+    case FMHA_ERR_ALIGNMENT: return "misaligned pointer";
+    case FMHA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case FMHA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

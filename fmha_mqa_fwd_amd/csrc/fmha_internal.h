@@ -1,0 +1,47 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernels.
+// Not installed; callers use include/fmha_mqa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fmha {
+
+enum OutMode : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_PARTIAL = 2 };
+
+// One launch of the attention kernel.  Rows r = (b*T + t)*n_h + h of q/out are
+// split into groups that share one K/V set: a batch (dense, T*n_h rows) or a
+// token (gather, n_h rows).  Row r belongs to group r / rows_per_group.
+struct FwdParams {
+  const uint16_t* q;        // bf16 [total_rows, hd]
+  const uint16_t* k;        // bf16 [n_groups, s_k, hd] (dense) or [pool_rows, hd]
+  const uint16_t* v;        // same layout as k
+  const int32_t* kv_idx;    // gather: int32 [n_groups, s_k]; dense: nullptr
+  void* out;                // OUT_F32/OUT_BF16: [total_rows, hd];
+                            // OUT_PARTIAL: fp32 [num_splits, total_rows, hd]
+  float* lse;               // [total_rows] or, partial, [num_splits, total_rows]
+  int64_t total_rows;
+  int rows_per_group;
+  int n_groups;
+  int tiles_per_group;      // filled in by launch_fwd for the chosen tile shape
+  int s_k;
+  int pool_rows;
+  int chunk;                // keys per split (== s_k when unsplit)
+  int num_splits;
+  int out_mode;             // OutMode
+  float scale_log2;         // softmax scale * log2(e)
+};
+
+// Picks the tile shape for hd / rows_per_group, sets p.tiles_per_group and
+// launches on `stream`.  Returns the launch status.
+hipError_t launch_fwd(FwdParams p, int hd, hipStream_t stream);
+
+// Number of workgroups launch_fwd would start (for the host-side size check).
+int64_t fwd_grid_size(const FwdParams& p, int hd);
+
+// out[r] = sum_i w_i o_i[r] / sum_i w_i with w_i = exp(lse_i[r] - max_i lse_i[r]).
+hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_parts,
+                        int rows, int hd, void* out, bool out_bf16, float* lse,
+                        hipStream_t stream);
+
+}  // namespace fmha

@@ -1,0 +1,111 @@
+/*
+ * fmha_mqa.h — multi-query attention forward for AMD MI355X (gfx950).
+ *
+ * C ABI of libfmha_mqa.so.  Every pointer argument named q/k/v/kv_idx/out/lse/
+ * o_parts/lse_parts/workspace is a DEVICE pointer allocated and owned by the
+ * caller; the library never allocates, frees or synchronises, keeps no state
+ * between calls, and launches all work asynchronously on the given stream
+ * (a hipStream_t passed as void*; NULL = the default stream).  Tensors are
+ * row-major and contiguous.  No C++ exception crosses this boundary: every
+ * function returns an fmha_status code, and validation happens before any
+ * launch (a non-OK status means nothing was enqueued).  Device faults, as for
+ * any HIP work, surface at the caller's next synchronisation.
+ *
+ * The operation is the fused attention forward of a DeepSeek-V4-style decoder
+ * as described on the dev-log pages of the "nvfp4-megamoe-kernel" project:
+ *   - QK^T -> softmax -> PV -> output, with the 1/sqrt(hd) scale applied in the
+ *     softmax to the unscaled dot product: page "CURRENT ISSUE: UMMA FMHA — Full
+ *     Pipeline + Production", sections "What's working" and "Key lessons from
+ *     this session";
+ *   - multi-query layout, K/V shared by every query head: page "May 24, 2026 —
+ *     Session Start Plan", section 3 "Start D2: Multi-Query Grid";
+ *   - O together with the row log-sum-exp: same page, "D1 Status Summary";
+ *   - more than one KV tile needs the running O rescaled: same page, section 2
+ *     "Test O Rescale at s_k > 128" and "Key Numbers" (8 tiles at top_k 1024);
+ *   - parts merged by O = sum_i exp(lse_i) O_i / sum_i exp(lse_i): page
+ *     "CURRENT ISSUE: UMMA FMHA — Full Pipeline + Production", "Next steps" 4;
+ *   - s_k = top_k keys selected from a KV store: "Key Numbers" and the
+ *     dsv4/kernels/cuda commit log (KV row gather, 32768-row compressed pool).
+ *
+ * Definition (per output row r = (b, t, h), natural log):
+ *   x_j   = scale * sum_d q[b,t,h,d] * K_j[d]
+ *   out[r] = sum_j softmax(x)_j * V_j          (normalised over the row's keys)
+ *   lse[r] = ln sum_j exp(x_j)
+ * with K_j, V_j = k[b,j], v[b,j] (dense) or k[kv_idx[b,t,j]], v[kv_idx[b,t,j]]
+ * (gather).  A row with no keys has out = 0 and lse = -inf.
+ */
+#ifndef FMHA_MQA_H
+#define FMHA_MQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FMHA_OK = 0,
+  FMHA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad dtype/scale/splits */
+  FMHA_ERR_UNSUPPORTED = 2, /* head dim not in {64, 128, 256}; sizes beyond int32 rows */
+  FMHA_ERR_ALIGNMENT = 3,   /* a tensor pointer not 16-byte aligned (lse: 4-byte) */
+  FMHA_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned */
+  FMHA_ERR_LAUNCH = 5       /* the HIP runtime rejected a kernel launch */
+} fmha_status;
+
+typedef enum { FMHA_F32 = 0, FMHA_BF16 = 1 } fmha_dtype;
+
+/* Bytes of workspace fmha_mqa_fwd needs for num_splits > 1 (0 when
+ * num_splits == 1): fp32 partial outputs [num_splits, B*T*n_h, hd] and fp32
+ * partial LSEs [num_splits, B*T*n_h], each region 256-byte aligned.
+ * Returns 0 as well for invalid arguments. */
+size_t fmha_mqa_workspace_bytes(int B, int T, int n_h, int hd, int num_splits);
+
+/* Attention forward.
+ *  q        bf16 [B, T, n_h, hd]
+ *  k, v     bf16 [B, s_k, hd] when kv_idx == NULL (dense: every query head of
+ *           batch b reads the same K/V rows), else bf16 pools [pool_rows, hd]
+ *  kv_idx   NULL, or int32 [B, T, s_k]: token (b, t) attends to pool rows
+ *           kv_idx[b, t, 0..s_k-1].  An entry outside [0, pool_rows) is never
+ *           read; that key is masked out (weight 0).
+ *  out      [B, T, n_h, hd] of out_dtype (FMHA_F32 or FMHA_BF16, RNE rounding)
+ *  lse      fp32 [B, T, n_h], natural log
+ *  B, T, n_h >= 0 (a zero gives an immediate FMHA_OK); s_k >= 0 (0: every row
+ *           empty, k/v/kv_idx may be NULL); hd in {64, 128, 256};
+ *  pool_rows  rows of the k/v pools (gather only; ignored when kv_idx == NULL)
+ *  scale    finite and > 0 (e.g. 1/sqrt(hd))
+ *  num_splits  1: one pass over the keys.  > 1 (at most max(s_k, 1)): split-KV —
+ *           the keys are cut into contiguous chunks of ceil(s_k/num_splits);
+ *           each chunk's normalised partial O and LSE go to the workspace and a
+ *           second kernel merges them (see fmha_lse_merge) into out/lse.
+ *  workspace   device memory of >= fmha_mqa_workspace_bytes(...) bytes,
+ *           16-byte aligned; may be NULL when num_splits == 1.
+ * q, k, v, out, workspace must be 16-byte aligned; kv_idx and lse 4-byte. */
+int fmha_mqa_fwd(const void* q, const void* k, const void* v,
+                 const int32_t* kv_idx, void* out, float* lse,
+                 int B, int T, int n_h, int s_k, int hd, int pool_rows,
+                 float scale, int out_dtype, int num_splits,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Log-sum-exp merge of normalised partial results (page "CURRENT ISSUE: UMMA
+ * FMHA — Full Pipeline + Production", "Next steps" 4):
+ *   M = max_i lse_i,  w_i = exp(lse_i - M),
+ *   out = sum_i w_i o_i / sum_i w_i,  lse = M + ln sum_i w_i.
+ *  o_parts    fp32 [n_parts, rows, hd], each part normalised over its keys
+ *  lse_parts  fp32 [n_parts, rows], natural log; -inf marks an empty part
+ *  out        [rows, hd] of out_dtype; lse fp32 [rows] (may be NULL: not written)
+ * A row whose parts are all empty gets out = 0, lse = -inf.
+ * n_parts >= 1, rows >= 0, hd >= 4 and a multiple of 4; o_parts and out
+ * 16-byte aligned (out 8-byte for bf16). */
+int fmha_lse_merge(const float* o_parts, const float* lse_parts, int n_parts,
+                   int rows, int hd, void* out, int out_dtype, float* lse,
+                   void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* fmha_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FMHA_MQA_H */

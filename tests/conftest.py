@@ -26,3 +26,13 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # Name the case on the real stderr before it touches the GPU, so a run that
+    # dies inside a kernel still says which case it was.
+    if "gpu" in request.keywords:
+        sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

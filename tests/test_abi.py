@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/fmha_mqa.h declares, and rejects bad arguments with the
+documented status before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fmha_mqa.h")
+
+
+def _lib_path():
+    path = os.path.join(ROOT, "fmha_mqa_fwd_amd", "libfmha_mqa.so")
+    if not os.path.exists(path):  # build only when nothing is built
+        from fmha_mqa_fwd_amd import build as b
+        b.build()
+    return path
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fmha_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == ["fmha_lse_merge", "fmha_mqa_fwd",
+                                     "fmha_mqa_workspace_bytes", "fmha_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    path = _lib_path()
+    lib = ctypes.CDLL(path)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True)
+    exported = {ln.split()[-1] for ln in nm.stdout.splitlines() if " T " in ln}
+    for name in _declared_functions():
+        assert name in exported, f"{name} is not a dynamic text symbol"
+
+
+def test_binding_covers_every_symbol():
+    _lib_path()
+    import fmha_mqa_fwd_amd as F
+    assert sorted(F.SIGNATURES) == _declared_functions()
+
+
+@pytest.fixture(scope="module")
+def F():
+    _lib_path()
+    import fmha_mqa_fwd_amd
+    return fmha_mqa_fwd_amd
+
+
+# fake, suitably aligned device addresses: validation must reject before any use
+A = 1 << 20
+
+
+def _fwd(F, **kw):
+    args = dict(q=A, k=A, v=A, kv_idx=None, out=A, lse=A, B=1, T=1, n_h=1, s_k=8, hd=64,
+                pool_rows=0, scale=0.125, out_dtype=0, num_splits=1, ws=None, ws_bytes=0,
+                stream=None)
+    args.update(kw)
+    return F.raw_fwd(args["q"], args["k"], args["v"], args["kv_idx"], args["out"], args["lse"],
+                     args["B"], args["T"], args["n_h"], args["s_k"], args["hd"],
+                     args["pool_rows"], args["scale"], args["out_dtype"], args["num_splits"],
+                     args["ws"], args["ws_bytes"], args["stream"])
+
+
+def test_status_strings(F):
+    assert F.status_string(0) == "ok"
+    assert "align" in F.status_string(3)
+    assert F.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hd=96), 2), (dict(hd=512), 2), (dict(hd=0), 2),
+    (dict(out_dtype=2), 1), (dict(B=-1), 1), (dict(s_k=-1), 1), (dict(num_splits=0), 1),
+    (dict(num_splits=9), 1), (dict(scale=0.0), 1), (dict(scale=-1.0), 1),
+    (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),
+    (dict(q=None), 1), (dict(out=None), 1), (dict(lse=None), 1), (dict(k=None), 1),
+    (dict(v=None), 1), (dict(kv_idx=A, pool_rows=0), 1),
+    (dict(q=A + 8), 3), (dict(k=A + 2), 3), (dict(out=A + 4), 3), (dict(lse=A + 2), 3),
+    (dict(kv_idx=A + 2, pool_rows=5), 3),
+    (dict(num_splits=2), 4), (dict(num_splits=2, ws=A, ws_bytes=16), 4),
+    (dict(num_splits=2, ws=A + 8, ws_bytes=1 << 30), 4),
+])
+def test_fwd_rejects_bad_arguments(F, kw, status):
+    assert _fwd(F, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(T=0), dict(n_h=0, q=None, out=None)])
+def test_fwd_empty_problem_is_a_no_op(F, kw):
+    # zero rows: nothing to launch, OK even with dangling pointers
+    assert _fwd(F, **kw) == 0
+
+
+def test_workspace_bytes(F):
+    assert F.workspace_bytes(32, 1, 128, 256, 1) == 0
+    rows = 32 * 128
+    o = 8 * rows * 256 * 4
+    l_ = 8 * rows * 4
+    r = lambda x: (x + 255) // 256 * 256
+    assert F.workspace_bytes(32, 1, 128, 256, 8) == r(o) + r(l_)
+    assert F.workspace_bytes(-1, 1, 1, 64, 2) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, A, 0, 4, 64, A, 0, A, None), 1),      # n_parts < 1
+    ((A, A, 2, 4, 62, A, 0, A, None), 1),      # hd not a multiple of 4
+    ((A, A, 2, -1, 64, A, 0, A, None), 1),
+    ((A, A, 2, 4, 64, A, 3, A, None), 1),      # bad dtype
+    ((None, A, 2, 4, 64, A, 0, A, None), 1),
+    ((A + 4, A, 2, 4, 64, A, 0, A, None), 3),
+    ((A, A, 2, 4, 64, A + 4, 0, A, None), 3),  # fp32 out needs 16 B
+    ((A, A, 2, 0, 64, None, 0, None, None), 0),  # no rows: no-op
+])
+def test_merge_rejects_bad_arguments(F, args, status):
+    assert F.raw_merge(*args) == status

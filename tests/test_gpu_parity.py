@@ -1,0 +1,263 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Bar (every case): max |O - O_ref| <= 1e-2, minimum per-row cosine >= 0.9999,
+max |lse - lse_ref| <= 1e-3, with O_ref, lse_ref from oracle.fp64 on the very
+bf16 inputs the GPU read.  Small and mid-size problems compare every row; the
+full-size workloads compare sampled rows (the oracle computes them one group at
+a time) and check properties of all rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MIN_COS, LSE_ERR = 1e-2, 0.9999, 1e-3
+
+
+@pytest.fixture(scope="module")
+def F():
+    import fmha_mqa_fwd_amd
+    return fmha_mqa_fwd_amd
+
+
+def _dt(name):
+    return torch.float32 if name == "f32" else torch.bfloat16
+
+
+def _run(F, q, k, v, idx, scale, out_dtype, num_splits):
+    dev = torch.device("cuda:0")
+    out, lse = F.fwd(q.to(dev), k.to(dev), v.to(dev), None if idx is None else idx.to(dev),
+                     scale=scale, out_dtype=out_dtype, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _check(out, lse, q, k, v, idx, scale, rows=None, bar=(MAX_ABS, MIN_COS, LSE_ERR)):
+    hd = q.shape[-1]
+    O_ref, L_ref = oracle.attention(q, k, v, scale, kv_idx=idx, rows=rows)
+    o = out.float().reshape(-1, hd)
+    l_ = lse.reshape(-1)
+    if rows is not None:
+        ri = torch.as_tensor(rows, device=o.device)
+        o, l_ = o[ri], l_[ri]
+    m = oracle.row_metrics(o.cpu().numpy(), O_ref, l_.cpu().numpy(), L_ref)
+    assert m["max_abs"] <= bar[0], m
+    assert m["min_row_cos"] >= bar[1], m
+    assert m["lse_err"] <= bar[2], m
+    return m
+
+
+def _case(F, w, rows=None):
+    q, k, v, idx = W.make_inputs(w)
+    out, lse = _run(F, q, k, v, idx, w.scale, _dt(w.out_dtype), w.num_splits)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    return _check(out, lse, q, k, v, idx, w.scale, rows=rows)
+
+
+# ------------------------------------------------------------ the workloads
+@pytest.mark.parametrize("cid", [1, 2])
+def test_small_workloads_all_rows(F, cid):
+    _case(F, W.get(cid))
+
+
+def test_mqa_decode_split8_all_rows(F):
+    _case(F, W.get(3))
+
+
+def _sample_rows(n_rows, n, seed):
+    g = np.random.default_rng(seed)
+    rows = g.choice(n_rows, size=n, replace=False)
+    return np.concatenate([[0, n_rows - 1], rows])
+
+
+def test_mqa_prefill_full_size_sampled(F):
+    w = W.get(4)
+    _case(F, w, rows=_sample_rows(w.rows, 510, 4))
+
+
+def test_sparse_topk_full_size_sampled(F):
+    w = W.get(5)
+    _case(F, w, rows=_sample_rows(w.rows, 382, 5))
+
+
+# ------------------------------------------------------------------ sweeps
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("s_k", [1, 7, 64, 129, 256, 1000])
+def test_head_dim_and_key_count_sweep(F, hd, s_k):
+    w = W.make_custom(B=2, T=3, n_h=37, hd=hd, s_k=s_k, out_dtype="f32", seed=hd * 7 + s_k)
+    _case(F, w)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("rows", [(1, 1, 1), (1, 129, 2), (3, 5, 64), (1, 2, 200), (2, 1, 300)])
+def test_ragged_row_counts(F, hd, rows):
+    B, T, n_h = rows
+    w = W.make_custom(B=B, T=T, n_h=n_h, hd=hd, s_k=300, out_dtype="bf16", seed=B * T * n_h + hd)
+    _case(F, w)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 13])
+@pytest.mark.parametrize("hd", [64, 128, 256])
+def test_split_kv(F, splits, hd):
+    w = W.make_custom(B=3, T=1, n_h=128, hd=hd, s_k=1000, out_dtype="bf16",
+                      num_splits=splits, seed=splits * 31 + hd)
+    _case(F, w)
+
+
+def test_split_with_empty_trailing_chunks(F):
+    # 9 keys in 8 chunks of 2: chunks 5..7 are empty (lse -inf) and must vanish
+    w = W.make_custom(B=2, T=1, n_h=16, hd=128, s_k=9, out_dtype="f32", num_splits=8, seed=9)
+    _case(F, w)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("n_h", [1, 16, 128, 200])
+def test_gather(F, hd, n_h):
+    w = W.make_custom(B=2, T=5, n_h=n_h, hd=hd, s_k=333, pool=4096, out_dtype="bf16",
+                      seed=hd + n_h)
+    _case(F, w)
+
+
+def test_gather_split(F):
+    w = W.make_custom(B=2, T=3, n_h=128, hd=128, s_k=1024, pool=8192, out_dtype="bf16",
+                      num_splits=4, seed=5)
+    _case(F, w)
+
+
+def test_gather_sorted_and_shuffled_indices_agree(F):
+    w = W.make_custom(B=1, T=4, n_h=64, hd=128, s_k=500, pool=2048, out_dtype="f32", seed=3)
+    q, k, v, idx = W.make_inputs(w)
+    o1, l1 = _run(F, q, k, v, idx, w.scale, torch.float32, 1)
+    srt = torch.sort(idx, dim=-1).values.contiguous()
+    o2, l2 = _run(F, q, k, v, srt, w.scale, torch.float32, 1)
+    _check(o2, l2, q, k, v, srt, w.scale)
+    assert (o1 - o2).abs().max().item() < 1e-3
+
+
+def test_gather_out_of_range_indices_are_masked(F):
+    """Entries outside [0, pool_rows) are never read and contribute nothing: the
+    result equals attention over the valid entries only."""
+    w = W.make_custom(B=1, T=3, n_h=32, hd=128, s_k=200, pool=1000, out_dtype="f32", seed=17)
+    q, k, v, idx = W.make_inputs(w)
+    bad = idx.clone()
+    bad[0, 0, 5] = -1
+    bad[0, 1, 100:150] = 1000
+    bad[0, 2, :] = 2 ** 31 - 1   # every entry of token 2 invalid: empty rows
+    out, lse = _run(F, q, k, v, bad, w.scale, torch.float32, 1)
+    # token 0 and 1: oracle on the valid subset
+    for t, keep in [(0, [j for j in range(200) if j != 5]),
+                    (1, [j for j in range(200) if not 100 <= j < 150])]:
+        sub = bad[:, t:t + 1, keep].contiguous()
+        _check(out[:, t:t + 1], lse[:, t:t + 1], q[:, t:t + 1], k, v, sub, w.scale)
+    assert torch.all(out[0, 2] == 0) and torch.all(torch.isneginf(lse[0, 2]))
+
+
+# ---------------------------------------------------- structure / adversarial
+def test_structured_inputs_catch_layout_swaps(F):
+    """Distinct, smooth values per (key, d) and per head: any swapped axis or
+    wrong key<->value pairing shows up far above the tolerance."""
+    B, T, n_h, hd, s_k = 1, 2, 64, 128, 384
+    j = torch.arange(s_k, dtype=torch.float32)[:, None]
+    d = torch.arange(hd, dtype=torch.float32)[None, :]
+    v = torch.sin(0.37 * j + 0.11 * d * d / hd + 0.5 * d).to(torch.bfloat16)[None]
+    k = (torch.cos(0.05 * j * (1 + d / hd)) * (1 + d / hd)).to(torch.bfloat16)[None]
+    h = torch.arange(n_h, dtype=torch.float32)[:, None]
+    q = torch.stack([torch.sin(0.3 * h + 0.07 * d * (t + 1)) * 3 for t in range(T)])
+    q = q.to(torch.bfloat16)[None]
+    scale = 1 / math.sqrt(hd)
+    out, lse = _run(F, q, k, v, None, scale, torch.float32, 1)
+    _check(out, lse, q, k, v, None, scale)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_logits_growing_tile_after_tile(F, splits):
+    """Row maxima rise in every KV tile (the O rescale runs at each tile), and
+    the last key dominates."""
+    B, T, n_h, hd, s_k = 1, 1, 128, 128, 1024
+    g = torch.Generator().manual_seed(1)
+    u = torch.randn(hd, generator=g)
+    a = torch.linspace(0.0, 3.0, s_k)
+    noise = 0.1 * torch.randn(s_k, hd, generator=g)
+    k = (a[:, None] * u[None, :] + noise)
+    k[-1] = 6.0 * u
+    q = (u[None, :] + 0.2 * torch.randn(n_h, hd, generator=g)).reshape(1, 1, n_h, hd)
+    v = torch.randn(1, s_k, hd, generator=g)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k[None], v))
+    scale = 1 / math.sqrt(hd)
+    out, lse = _run(F, q, k, v, None, scale, torch.float32, splits)
+    _check(out, lse, q, k, v, None, scale)
+
+
+def test_large_magnitude_inputs_stay_finite(F):
+    w = W.make_custom(B=1, T=4, n_h=64, hd=128, s_k=512, out_dtype="f32", scale_in=8.0, seed=8)
+    q, k, v, idx = W.make_inputs(w)
+    out, lse = _run(F, q, k, v, idx, w.scale, torch.float32, 1)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    assert lse.abs().max().item() > 100
+    _check(out, lse, q, k, v, idx, w.scale)
+
+
+def test_single_key_returns_that_value_row(F):
+    w = W.make_custom(B=2, T=3, n_h=50, hd=128, s_k=1, out_dtype="f32", seed=1)
+    q, k, v, _ = W.make_inputs(w)
+    out, lse = _run(F, q, k, v, None, w.scale, torch.float32, 1)
+    ref = v.float()[:, None, None, 0, :].expand(out.shape)   # O = V_0 exactly
+    assert torch.equal(out.cpu(), ref)
+    _check(out, lse, q, k, v, None, w.scale)
+
+
+def test_zero_keys_gives_empty_rows(F):
+    dev = torch.device("cuda:0")
+    q = torch.randn(1, 2, 4, 64).to(torch.bfloat16).to(dev)
+    k = torch.empty(1, 0, 64, dtype=torch.bfloat16, device=dev)
+    out, lse = F.fwd(q, k, k.clone(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_repeat_runs_are_bitwise_identical(F):
+    w = W.make_custom(B=2, T=16, n_h=64, hd=128, s_k=1024, out_dtype="bf16", num_splits=2, seed=2)
+    q, k, v, idx = W.make_inputs(w)
+    o1, l1 = _run(F, q, k, v, idx, w.scale, torch.bfloat16, 2)
+    o2, l2 = _run(F, q, k, v, idx, w.scale, torch.bfloat16, 2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_runs_on_a_side_stream(F):
+    w = W.make_custom(B=1, T=8, n_h=64, hd=128, s_k=256, out_dtype="f32", seed=6)
+    q, k, v, _ = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out, lse = F.fwd(qd, kd, vd, out_dtype=torch.float32)
+    s.synchronize()
+    _check(out, lse, q, k, v, None, w.scale)
+
+
+# --------------------------------------------------------------- the merge
+@pytest.mark.parametrize("hd,out_dtype", [(64, "f32"), (128, "bf16"), (256, "f32"), (20, "f32")])
+def test_lse_merge_entry_point(F, hd, out_dtype):
+    g = np.random.default_rng(hd)
+    P, R = 5, 333
+    o = (0.25 * g.standard_normal((P, R, hd))).astype(np.float32)  # |o| < 2: bf16 half-ulp < 1e-2
+    lse = (g.standard_normal((P, R)) * 5).astype(np.float32)
+    lse[2, ::7] = -np.inf
+    o[2, ::7] = np.nan          # an empty part's O is never read
+    lse[:, 10] = -np.inf        # a row whose parts are all empty
+    dev = torch.device("cuda:0")
+    out, L = F.lse_merge(torch.from_numpy(o).to(dev), torch.from_numpy(lse).to(dev),
+                         out_dtype=_dt(out_dtype))
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.lse_merge(np.where(np.isneginf(lse)[:, :, None], 0.0, o), lse)
+    m = oracle.row_metrics(out.float().cpu().numpy(), Oref, L.cpu().numpy(), Lref)
+    assert m["max_abs"] <= (1e-2 if out_dtype == "bf16" else 1e-5), m
+    assert m["lse_err"] <= 1e-5, m
+    assert torch.all(out[10] == 0) and torch.isneginf(L[10])
