@@ -1,0 +1,332 @@
+"""Benchmark of the MQA attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path, each part on its own batch of
+seeded synthetic input already resident in HBM:
+  * mqa_prefill  B=2 T=4096 n_h=64 hd=128 s_k=1024 (bf16 out)  — the headline:
+    attention TFLOP/s against the bf16 dense MFMA peak;
+  * mqa_decode   B=32 T=1 n_h=128 hd=256 s_k=1024, 8-way split-KV + LSE merge
+    (bf16 out) — HBM GB/s of algorithmic bytes against the HBM peak;
+  * sparse_topk  B=4 T=512 n_h=128 hd=128, 1024 of 32768 pool rows gathered per
+    token (bf16 out) — TFLOP/s and gathered GB/s.
+Each call is timed with its own pair of HIP events on the launch stream, with
+L2 and the memory-side cache flushed (a 512 MiB write) before every timed call,
+so every call reads its inputs from HBM.  Back-to-back ("warm") times are
+reported beside them.  Rank 0 prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+FLUSH_BYTES = 512 << 20
+
+# Sources the committed HBM traffic counters were taken on; a changed kernel
+# source makes those counters stale and the traffic field null.
+KERNEL_SOURCES = ["fmha_mqa_fwd_amd/csrc/fmha_fwd.hip", "fmha_mqa_fwd_amd/csrc/lse_merge.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+# which attention kernels (by demangled name) serve each workload
+WORKLOAD_KERNEL_SIG = {
+    "mqa_prefill": lambda k: "fwd_kernel<128" in k and "false>" in k,
+    "mqa_decode": lambda k: "fwd_kernel<256" in k or "merge_kernel" in k,
+    "sparse_topk": lambda k: "fwd_kernel<128" in k and "true>" in k,
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """Per-launch HBM bytes (FETCH+WRITE, copy-calibrated) for `workload` from
+    the committed counter file, or None when absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    ent = rec.get("workloads", {}).get(workload)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+CASES = (("mqa_prefill", 4), ("mqa_decode", 3), ("sparse_topk", 5))
+COPY_BYTES = 256 << 20   # calibration copy: reads and writes this many bytes
+
+
+class Case:
+    def __init__(self, cid, dev):
+        import fmha_mqa_fwd_amd as F
+
+        self.F = F
+        self.w = W.get(cid)
+        q, k, v, idx = W.make_inputs(self.w)
+        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        self.idx = None if idx is None else idx.to(dev)
+        self.out_dtype = torch.float32 if self.w.out_dtype == "f32" else torch.bfloat16
+        w = self.w
+        self.out = torch.empty((w.B, w.T, w.n_h, w.hd), dtype=self.out_dtype, device=dev)
+        self.lse = torch.empty((w.B, w.T, w.n_h), dtype=torch.float32, device=dev)
+        nb = F.workspace_bytes(w.B, w.T, w.n_h, w.hd, w.num_splits)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+
+    def __call__(self):
+        self.F.fwd(self.q, self.k, self.v, self.idx, scale=self.w.scale,
+                   out_dtype=self.out_dtype, num_splits=self.w.num_splits,
+                   out=self.out, lse=self.lse, workspace=self.ws)
+
+
+def time_case(case, steps, warmup, flush_buf):
+    """Mean per-call time in ms: flushed (events around each call, cache
+    flushed before it) and warm (events around `steps` back-to-back calls)."""
+    for _ in range(warmup):
+        case()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        flush_buf.fill_(i & 0xFF)
+        starts[i].record()
+        case()
+        ends[i].record()
+    torch.cuda.synchronize()
+    flushed = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        case()
+    e1.record()
+    torch.cuda.synchronize()
+    warm = e0.elapsed_time(e1) / steps
+    flushed.sort()
+    return {"ms": sum(flushed) / len(flushed), "ms_median": flushed[len(flushed) // 2],
+            "ms_p10": flushed[len(flushed) // 10], "ms_p90": flushed[(9 * len(flushed)) // 10],
+            "ms_warm": warm}
+
+
+def profile_mode(args, dev):
+    """Runs one workload `warmup + steps` times back to back (and, with
+    --copy-calibration, `steps` plain copies of COPY_BYTES) for a profiler."""
+    names = [n for n, _ in CASES] if args.only == "all" else [args.only]
+    for name in names:
+        case = Case(dict(CASES)[name], dev)
+        for _ in range(args.warmup + args.steps):
+            case()
+        torch.cuda.synchronize()
+        del case
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] profile mode done: {args.only} x{args.warmup + args.steps}",
+          file=sys.stderr, flush=True)
+
+
+def _counter_rows(d):
+    """(kernel name, counter name, value) per dispatch from a rocprofv3 --pmc
+    output directory (its *counter_collection.csv)."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    out = []
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                out.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]),
+                            r.get("Dispatch_Id")))
+    return out
+
+
+def ingest_counters(fetch_dir, write_dir):
+    """Per-launch HBM bytes of each attention kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for a plain copy of COPY_BYTES (expected COPY_BYTES/1024 KiB each way)."""
+    rec = {"kernel_source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES,
+           "workloads": {}, "kernels": {}}
+    scale = {}
+    per_kernel = {}
+    for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        sums = {}
+        for kname, cn, val, disp in _counter_rows(d):
+            if cn != cname:
+                continue
+            sums.setdefault(kname, []).append(val)
+        copies = [v for k, vs in sums.items()
+                  if "copy" in k.lower() and "fill" not in k.lower() for v in vs]
+        if not copies:
+            raise SystemExit(f"no copy-kernel dispatch found in {d}")
+        copy_kib = sorted(copies)[len(copies) // 2]
+        scale[cname] = (COPY_BYTES / 1024.0) / copy_kib
+        for k, vs in sums.items():
+            if "fmha" in k:
+                per_kernel.setdefault(k, {})[cname] = sorted(vs)[len(vs) // 2]
+    for k, c in per_kernel.items():
+        kib_f, kib_w = c.get("FETCH_SIZE", 0.0), c.get("WRITE_SIZE", 0.0)
+        rec["kernels"][k] = {
+            "fetch_kib_raw": kib_f, "write_kib_raw": kib_w,
+            "bytes_per_launch": kib_f * 1024 * scale["FETCH_SIZE"] + kib_w * 1024 * scale["WRITE_SIZE"]}
+    rec["copy_scale"] = scale
+    # map kernels to workloads: the attention kernel with the largest traffic
+    # of each workload's run is recorded by its template signature
+    for name, _ in CASES:
+        sig = WORKLOAD_KERNEL_SIG.get(name)
+        tot = sum(v["bytes_per_launch"] for k, v in rec["kernels"].items() if sig and sig(k))
+        if tot:
+            rec["workloads"][name] = {"bytes_per_launch": tot}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def cpu_baseline(budget_s=12.0):
+    """The float64 oracle on a bounded sample of the prefill workload's rows,
+    on this host's cores; returns its attention TFLOP/s."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    w = W.get(4)
+    q, k, v, idx = W.make_inputs(w)
+    rng = np.random.default_rng(0)
+    oracle.attention(q, k, v, w.scale, rows=np.arange(1024))       # warm the BLAS pool
+    n = 16384
+    t = time.perf_counter()
+    oracle.attention(q, k, v, w.scale, rows=rng.choice(w.rows, n, replace=False))
+    dt = time.perf_counter() - t
+    n = int(min(w.rows, max(n, n * budget_s / max(dt, 1e-3))))
+    rows = rng.choice(w.rows, n, replace=False)
+    t = time.perf_counter()
+    oracle.attention(q, k, v, w.scale, rows=rows)
+    dt = time.perf_counter() - t
+    flops = 4.0 * n * w.s_k * w.hd
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {w.rows} rows of {w.describe()} (float64 numpy), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=[n for n, _ in CASES] + ["all"],
+                    help="profile mode: run one workload back to back, no JSON line")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="profile mode: also run a plain device copy of known size")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "--only ... --copy-calibration into " + TRAFFIC_FILE)
+    args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention shards by batch/token with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    if args.only:
+        profile_mode(args, dev)
+        return
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    res = {}
+    for name, cid in CASES:
+        case = Case(cid, dev)
+        t = time_case(case, args.steps, args.warmup, flush_buf)
+        w = case.w
+        t["flops"] = w.flops
+        t["bytes"] = w.algorithmic_bytes()
+        t["tflops"] = w.flops / (t["ms"] * 1e-3) / 1e12
+        t["gbps"] = w.algorithmic_bytes() / (t["ms"] * 1e-3) / 1e9
+        t["workload"] = w.describe()
+        res[name] = t
+        print(f"[bench] {name}: {t['ms'] * 1e3:.1f} us/call flushed "
+              f"({t['ms_warm'] * 1e3:.1f} warm), {t['tflops']:.1f} TFLOP/s, "
+              f"{t['gbps']:.0f} GB/s", file=sys.stderr, flush=True)
+        del case
+        torch.cuda.empty_cache()
+
+    p, d, s = res["mqa_prefill"], res["mqa_decode"], res["sparse_topk"]
+    traffic = committed_traffic("mqa_prefill")
+    line = {
+        "metric": "attention TFLOP/s (prefill) + HBM GB/s (decode), % of MI355X peak, hd=128/256",
+        "value": round(p["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(p["ms"] + d["ms"] + s["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": p["workload"], "step": "mqa_prefill + mqa_decode + sparse_topk",
+                   "global_batch": 2, "seq_len": 4096, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(p["tflops"], 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "decode": {"value": round(d["gbps"], 1), "unit": "GB/s",
+                   "frac_of_hbm_peak": round(d["gbps"] / PEAK_HBM_GBPS, 4),
+                   "us_per_call": round(d["ms"] * 1e3, 2),
+                   "us_per_call_warm": round(d["ms_warm"] * 1e3, 2),
+                   "algorithmic_bytes": d["bytes"], "workload": d["workload"],
+                   "traffic": committed_traffic("mqa_decode")},
+        "sparse_topk": {"value": round(s["tflops"], 2), "unit": "TFLOP/s",
+                        "frac_of_mfma_peak": round(s["tflops"] / PEAK_BF16_TFLOPS, 4),
+                        "gathered_GBps": round(s["gbps"], 1),
+                        "us_per_call": round(s["ms"] * 1e3, 2),
+                        "us_per_call_warm": round(s["ms_warm"] * 1e3, 2),
+                        "workload": s["workload"]},
+        "prefill_detail": {"us_per_call": round(p["ms"] * 1e3, 2),
+                           "us_median": round(p["ms_median"] * 1e3, 2),
+                           "us_p10": round(p["ms_p10"] * 1e3, 2),
+                           "us_p90": round(p["ms_p90"] * 1e3, 2),
+                           "us_per_call_warm": round(p["ms_warm"] * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -194,21 +194,27 @@ def test_logits_growing_tile_after_tile(F, splits):
     _check(out, lse, q, k, v, None, scale)
 
 
-def test_large_magnitude_inputs_stay_finite(F):
-    w = W.make_custom(B=1, T=4, n_h=64, hd=128, s_k=512, out_dtype="f32", scale_in=8.0, seed=8)
-    q, k, v, idx = W.make_inputs(w)
-    out, lse = _run(F, q, k, v, idx, w.scale, torch.float32, 1)
+def test_large_magnitude_logits_stay_finite(F):
+    """q, k ~ N(0, 8^2): logits of a few hundred, softmax nearly one-hot; the
+    max-shifted exponentials must neither overflow nor lose the row."""
+    w = W.make_custom(B=1, T=4, n_h=64, hd=128, s_k=512, out_dtype="f32", seed=8)
+    q, k, v, _ = W.make_inputs(w)
+    q = (q.float() * 8).to(torch.bfloat16)
+    k = (k.float() * 8).to(torch.bfloat16)
+    out, lse = _run(F, q, k, v, None, w.scale, torch.float32, 1)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     assert lse.abs().max().item() > 100
-    _check(out, lse, q, k, v, idx, w.scale)
+    _check(out, lse, q, k, v, None, w.scale)
 
 
 def test_single_key_returns_that_value_row(F):
+    """s_k = 1: O = V_0.  The kernel folds scale*log2(e) into an FMA, so the
+    lone weight is 1 within fp32 rounding, not bit-exactly."""
     w = W.make_custom(B=2, T=3, n_h=50, hd=128, s_k=1, out_dtype="f32", seed=1)
     q, k, v, _ = W.make_inputs(w)
     out, lse = _run(F, q, k, v, None, w.scale, torch.float32, 1)
-    ref = v.float()[:, None, None, 0, :].expand(out.shape)   # O = V_0 exactly
-    assert torch.equal(out.cpu(), ref)
+    ref = v.float()[:, None, None, 0, :].expand(out.shape)
+    torch.testing.assert_close(out.cpu(), ref, rtol=1e-6, atol=0)
     _check(out, lse, q, k, v, None, w.scale)
 
 
