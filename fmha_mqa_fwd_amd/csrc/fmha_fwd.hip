@@ -8,7 +8,7 @@
 //     session");
 //   * multi-query: every query head of a batch/token reads one shared K/V head
 //     (page "May 24, 2026 — Session Start Plan", 3 "Start D2: Multi-Query Grid");
-//   * keys processed tile by tile with the running O rescaled whenever the row
+//   * keys processed tile by tile with the running O rescaled when the row
 //     maximum grows (same page, 2 "Test O Rescale at s_k > 128");
 //   * O and the row log-sum-exp as outputs (same page, "D1 Status Summary");
 //   * optional row gather of the s_k = top_k selected keys from a KV pool (same
@@ -18,19 +18,28 @@
 //   * Head-packed M: the rows of a group (all (t, h) of a batch, or all heads of
 //     a token) share K/V, so a workgroup takes WAVES*QW consecutive rows and
 //     every K/V tile staged in LDS serves all of them.
-//   * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: K (A operand) comes from LDS,
-//     Q^T (B operand) stays in VGPRs for the whole kernel.  In the 32x32
-//     accumulator layout lane l holds query column l%32 and 16 of the 32 keys,
-//     so a row's max/sum is an in-lane reduction plus one exchange with lane
-//     l^32, and the per-row rescale factor is a per-lane scalar.
-//   * O^T = V^T . P^T: the S^T accumulators, rounded to bf16, are already the B
-//     operand of the PV MFMA (no LDS round trip for P).  V^T is written to LDS
-//     transposed while staging, in the key order that the accumulator layout
-//     implies, so the A operand is one 16-byte LDS read.
-//   * Online softmax in base 2: x*scale*log2(e) folded into one FMA, exp2 on
-//     the hardware transcendental unit, fp32 row max/sum.
-//   * LDS tiles use an XOR swizzle of 16-byte chunks so the MFMA operand reads
-//     and the staging writes do not collide on banks.
+//   * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: K (A operand) from LDS, Q^T
+//     (B operand) in VGPRs for the whole kernel.  In the 32x32 accumulator
+//     layout lane l holds query column l%32 and 16 of the 32 keys, so a row's
+//     max/sum is an in-lane reduction plus one v_permlane32_swap, and the
+//     per-row rescale factor is a per-lane scalar.
+//   * O^T = V^T . P^T: the S^T accumulators, rounded to bf16, are the B operand
+//     of the PV MFMA as they stand (P never leaves registers).  V stays
+//     row-major in LDS; its A operand is read with ds_read_b64_tr_b16, whose
+//     16-lane transpose yields, for lane (d, half h), the keys that lane half h
+//     holds in S^T — in the same order.
+//   * Online softmax in base 2: x*scale*log2(e) folded into one FMA, exp2 on the
+//     transcendental unit, and a lazy rescale: the running maximum used for the
+//     exponentials only moves when a row's maximum grows by more than 2^8, so
+//     O and l are rescaled on a few tiles instead of every tile (exact: O and l
+//     always share the maximum they were computed against).
+//   * K/V tiles are double-buffered in LDS; the next tile's global loads are
+//     issued into registers before the current tile's MFMAs and written to the
+//     other buffer after them, so one barrier per tile suffices and load
+//     latency hides behind compute.  Two workgroups share a CU where registers
+//     allow, so one wave's softmax overlaps another's MFMAs.
+//   * LDS rows use XOR swizzles of 16-byte chunks chosen so that the MFMA operand
+//     reads and the staging writes are free of bank conflicts.
 #include <math.h>
 
 #include "fmha_internal.h"
@@ -39,31 +48,44 @@ namespace fmha {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-constexpr int WAVES = 4;
-constexpr int THREADS = WAVES * 64;
-constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+// The running max moves only when a row max exceeds it by more than this
+// (log2 units): exponentials then stay <= 2^8, far inside fp32/bf16 range.
+constexpr float RESCALE_THRESHOLD = 8.0f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
-// Physical 16-byte chunk for logical chunk c of LDS row `row`, for rows of CPR
-// chunks.  16+ chunks per row: XOR the low 4 bits with row ^ row>>3 (rows that
-// an MFMA operand read touches together, 32 consecutive rows, and the rows a
-// transposed staging write touches, rows 8 apart, both land on distinct
-// chunks).  8 chunks per row (128-byte rows, two per 256 bytes): XOR with
-// (row & 7) ^ (row>>3 & 1).
+// Swizzle of the 16-byte chunk index for K rows (A operand of S^T read with
+// ds_read_b128: 16 consecutive rows at one logical chunk must hit 16 distinct
+// bank groups; staging writes fill one row's chunks per 16 threads).
 template <int CPR>
-__device__ __forceinline__ int swz(int row) {
-  static_assert(CPR >= 8, "LDS rows must hold at least 8 chunks");
+__device__ __forceinline__ int swz_k(int row) {
   if constexpr (CPR >= 16) {
     return (row ^ (row >> 3)) & 15;
   } else {
     return (row & 7) ^ ((row >> 3) & 1);
+  }
+}
+
+// Swizzle for V rows, read by ds_read_b64_tr_b16: a 16-lane group reads 4
+// consecutive rows x 32 bytes (two chunks); the two groups of a wave half read
+// the neighbouring 32 bytes of the same rows.  The XOR values put the 4 rows'
+// chunk pairs (and quads) on distinct banks.
+template <int CPR>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (CPR >= 16) {
+    constexpr int f[4] = {0, 6, 10, 12};
+    return f[row & 3];
+  } else {
+    constexpr int f[4] = {0, 6, 4, 2};
+    return f[row & 3];
   }
 }
 
@@ -83,29 +105,43 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* s) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// Value of lane l^32 combined with this lane's: max and sum across the halves.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Key (within a 32-key block) held by accumulator register r of a lane in
-// half `hlf` of the wave, for the 32x32 MFMA output layout (rows grouped in
-// fours: register r covers row 8*(r/4) + 4*hlf + r%4, column lane%32).
+// half `hlf`, for the 32x32 MFMA output layout: register r covers row
+// 8*(r/4) + 4*hlf + r%4 at column lane%32.
 __device__ __forceinline__ int acc_row(int r, int hlf) {
   return 8 * (r >> 2) + 4 * hlf + (r & 3);
 }
 
-template <int HD, int QW, int KT, bool GATHER>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int HD, int QW, int KT, int WAVES, bool GATHER, int WPE>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(FwdParams p) {
+  constexpr int THREADS = WAVES * 64;
   constexpr int NQB = QW / 32;   // 32-query MFMA column blocks per wave
   constexpr int NDS = HD / 16;   // 16-wide contraction steps of QK^T
   constexpr int NKB = KT / 32;   // 32-key row blocks of S^T per tile
   constexpr int NKS = KT / 16;   // 16-key contraction steps of PV per tile
   constexpr int NDB = HD / 32;   // 32-wide d blocks of O^T
-  constexpr int K_CPR = HD / 8;  // 16-byte chunks per K row in LDS
-  constexpr int V_CPR = KT / 8;  // 16-byte chunks per V^T row in LDS
+  constexpr int CPR = HD / 8;    // 16-byte chunks per K/V row
   constexpr int M_WG = WAVES * QW;
+  constexpr int TILE_CH = KT * CPR;            // chunks per K (or V) tile
+  constexpr int CPT = TILE_CH / THREADS;       // chunks per thread per tile
+  constexpr int ROWS_PER_PASS = THREADS / CPR;
   static_assert(QW % 32 == 0 && KT % 32 == 0 && HD % 32 == 0, "tile shape");
+  static_assert(TILE_CH % THREADS == 0 && THREADS % CPR == 0, "staging shape");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[KT * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[HD * KT];
-  __shared__ int sIdx[KT];  // pool row per tile key, -1 = masked
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][KT * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][KT * HD];
+  __shared__ int sValid[GATHER ? 2 : 1][KT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -121,8 +157,58 @@ void fwd_kernel(FwdParams p) {
 
   const int key_lo = split * p.chunk;
   const int key_hi = min(key_lo + p.chunk, p.s_k);
+  const int n_tiles = key_hi > key_lo ? (key_hi - key_lo + KT - 1) / KT : 0;
   const int row0 = tile * M_WG + wave * QW;  // first row of this wave in its group
   const int64_t grow0 = (int64_t)group * p.rows_per_group;
+  const uint16_t* kbase = GATHER ? p.k : p.k + (int64_t)group * p.s_k * HD;
+  const uint16_t* vbase = GATHER ? p.v : p.v + (int64_t)group * p.s_k * HD;
+  const int32_t* ibase = GATHER ? p.kv_idx + (int64_t)group * p.s_k : nullptr;
+
+  // Staging assignment: chunk `sc` of rows srow0 + ROWS_PER_PASS*i.
+  const int sc = tid % CPR;
+  const int srow0 = tid / CPR;
+
+  // Global loads of one tile's K and V chunks into registers (zeros for keys
+  // outside [key_lo, key_hi) or with an out-of-range pool index).
+  u32x4 rk[CPT], rv[CPT];
+  int rvalid[CPT];
+  auto load_tile = [&](int t) {
+    const int t0 = key_lo + t * KT;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int row = srow0 + ROWS_PER_PASS * i;
+      const int key = t0 + row;
+      int64_t off = (int64_t)key * HD;
+      bool ok = key < key_hi;
+      if constexpr (GATHER) {
+        const int idx = ok ? ibase[key] : -1;
+        ok = ok && idx >= 0 && idx < p.pool_rows;
+        off = (int64_t)idx * HD;
+      }
+      rvalid[i] = ok;
+      rk[i] = u32x4{0u, 0u, 0u, 0u};
+      rv[i] = u32x4{0u, 0u, 0u, 0u};
+      if (ok) {
+        rk[i] = *reinterpret_cast<const u32x4*>(kbase + off + 8 * sc);
+        rv[i] = *reinterpret_cast<const u32x4*>(vbase + off + 8 * sc);
+      }
+    }
+  };
+  // Returns nonzero when this thread saw a masked key (gather only).
+  auto store_tile = [&](int buf) {
+    int masked = 0;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int row = srow0 + ROWS_PER_PASS * i;
+      *reinterpret_cast<u32x4*>(&sK[buf][row * HD + 8 * (sc ^ swz_k<CPR>(row))]) = rk[i];
+      *reinterpret_cast<u32x4*>(&sV[buf][row * HD + 8 * (sc ^ swz_v<CPR>(row))]) = rv[i];
+      if constexpr (GATHER) {
+        if (sc == 0) sValid[buf][row] = rvalid[i];
+      }
+      masked |= !rvalid[i];
+    }
+    return masked;
+  };
 
   // Q^T fragments (B operand of S^T = K.Q^T): lane (hlf, l32) of column block
   // qb holds q[row l32][16*ds + 8*hlf .. +7] for every contraction step ds.
@@ -147,87 +233,35 @@ void fwd_kernel(FwdParams p) {
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[db][qb][i] = 0.f;
-  float m[NQB], l[NQB];
+  float m[NQB], l[NQB];  // running max (scaled, log2 units) and partial row sum
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     m[qb] = neg_inf();
     l[qb] = 0.f;
   }
-
   const float c = p.scale_log2;
 
-  for (int t0 = key_lo; t0 < key_hi; t0 += KT) {
-    __syncthreads();  // every wave is done with the previous tile's LDS
+  // V operand read offsets (bytes within a tile) for ds_read_b64_tr_b16: lane
+  // (jj = lane%16, dsub = lane/16%2, hlf) of K-step ks, d block db, half r reads
+  // row 16*ks + 8*r + 4*hlf + jj/4, columns d0 + 4*(jj%4) .. +3, d0 = 32*db + 16*dsub.
+  const int jj = lane & 15;
+  const int dsub = (lane >> 4) & 1;
 
-    // ---- which pool row (gather) or key (dense) each tile row holds
-    int masked = 0;
-    if constexpr (GATHER) {
-      for (int j = tid; j < KT; j += THREADS) {
-        const int key = t0 + j;
-        int idx = -1;
-        if (key < key_hi) {
-          idx = p.kv_idx[(int64_t)group * p.s_k + key];
-          if (idx < 0 || idx >= p.pool_rows) idx = -1;
-        }
-        sIdx[j] = idx;
-        masked |= (idx < 0);
-      }
-      masked = __syncthreads_or(masked);
-    } else {
-      masked = (t0 + KT > key_hi);
-      for (int j = tid; j < KT; j += THREADS) sIdx[j] = (t0 + j < key_hi) ? 0 : -1;
-      __syncthreads();
-    }
+  int tile_masked = 0;
+  if (n_tiles > 0) {
+    load_tile(0);
+    const int mk = store_tile(0);
+    tile_masked = GATHER ? __syncthreads_or(mk) : (__syncthreads(), 0);
+  }
 
-    // ---- K tile: [KT rows][HD], row j = key t0+j, 16-byte chunks swizzled
-    for (int u = tid; u < KT * K_CPR; u += THREADS) {
-      const int row = u / K_CPR;
-      const int ch = u % K_CPR;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      const int idx = sIdx[row];
-      if (idx >= 0) {
-        const uint16_t* src = GATHER ? p.k + (int64_t)idx * HD
-                                     : p.k + ((int64_t)group * p.s_k + t0 + row) * HD;
-        w = *reinterpret_cast<const u32x4*>(src + 8 * ch);
-      }
-      *reinterpret_cast<u32x4*>(sK + row * HD + 8 * (ch ^ swz<K_CPR>(row))) = w;
-    }
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    const int t0 = key_lo + t * KT;
+    const bool have_next = t + 1 < n_tiles;
+    if (have_next) load_tile(t + 1);
 
-    // ---- V^T tile: [HD rows][KT keys].  Chunk (2*ks + hh) of row d holds the
-    // keys 16*ks + 8*(e/4) + 4*hh + e%4, e = 0..7: exactly the keys that lanes
-    // of half hh hold, in register order, in S^T's accumulators.
-    for (int u = tid; u < (HD / 8) * NKS * 2; u += THREADS) {
-      const int dc = u % (HD / 8);
-      const int rest = u / (HD / 8);
-      const int hh = rest & 1;
-      const int ks = rest >> 1;
-      u32x4 in[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 16 * ks + 8 * (e >> 2) + 4 * hh + (e & 3);
-        const int idx = sIdx[j];
-        in[e] = u32x4{0u, 0u, 0u, 0u};
-        if (idx >= 0) {
-          const uint16_t* src = GATHER ? p.v + (int64_t)idx * HD
-                                       : p.v + ((int64_t)group * p.s_k + t0 + j) * HD;
-          in[e] = *reinterpret_cast<const u32x4*>(src + 8 * dc);
-        }
-      }
-      const int cv = 2 * ks + hh;
-#pragma unroll
-      for (int di = 0; di < 8; ++di) {
-        u32x4 w;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const uint32_t lo = in[2 * a][di >> 1];
-          const uint32_t hi = in[2 * a + 1][di >> 1];
-          w[a] = (di & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        const int d = 8 * dc + di;
-        *reinterpret_cast<u32x4*>(sVt + d * KT + 8 * (cv ^ swz<V_CPR>(d))) = w;
-      }
-    }
-    __syncthreads();
+    const uint16_t* sk = sK[buf];
+    const uint16_t* sv = sV[buf];
 
     // ---- S^T = K . Q^T  (unscaled dot products, fp32)
     f32x16 s[NKB][NQB];
@@ -244,25 +278,28 @@ void fwd_kernel(FwdParams p) {
         const int row = 32 * kb + l32;
         const int ch = 2 * ds + hlf;
         const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(sK + row * HD + 8 * (ch ^ swz<K_CPR>(row)));
+            *reinterpret_cast<const bf16x8*>(sk + row * HD + 8 * (ch ^ swz_k<CPR>(row)));
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
           s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ds], s[kb][qb], 0, 0, 0);
       }
     }
-    if (masked) {
+    const bool dense_tail = !GATHER && (t0 + KT > key_hi);
+    if (dense_tail || (GATHER && tile_masked)) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if (sIdx[32 * kb + acc_row(r, hlf)] < 0) {
+          const int kr = 32 * kb + acc_row(r, hlf);
+          const bool ok = GATHER ? (sValid[buf][kr] != 0) : (t0 + kr < key_hi);
+          if (!ok) {
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) s[kb][qb][r] = neg_inf();
           }
         }
     }
 
-    // ---- online softmax (base 2) and O rescale
+    // ---- online softmax (base 2) with lazy rescale
     bf16x8 pf[NQB][NKS];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -271,10 +308,20 @@ void fwd_kernel(FwdParams p) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m[qb], mx * c);
-      const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_use);
+      const float m_tile = pair_max(mx) * c;
+      if (__any(m_tile > m[qb] + RESCALE_THRESHOLD)) {
+        const float m_new = fmaxf(m[qb], m_tile);
+        const float m_old_use = (m[qb] == neg_inf()) ? m_new : m[qb];
+        const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(m_old_use - m_new);
+        const float a0 = (m[qb] == neg_inf()) ? 0.f : alpha;
+        l[qb] *= a0;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][qb][i] *= a0;
+        m[qb] = m_new;
+      }
+      const float m_use = (m[qb] == neg_inf()) ? 0.f : m[qb];
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -287,12 +334,7 @@ void fwd_kernel(FwdParams p) {
         pf[qb][2 * kb] = pack_bf16x8(pv);
         pf[qb][2 * kb + 1] = pack_bf16x8(pv + 8);
       }
-      l[qb] = l[qb] * alpha + ls;
-      m[qb] = m_new;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][qb][i] *= alpha;
+      l[qb] += ls;
     }
 
     // ---- O^T += V^T . P^T
@@ -300,21 +342,34 @@ void fwd_kernel(FwdParams p) {
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int d = 32 * db + l32;
-        const int ch = 2 * ks + hlf;
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(sVt + d * KT + 8 * (ch ^ swz<V_CPR>(d)));
+        const int d = 32 * db + 16 * dsub + 4 * (jj & 3);
+        i16x4 part[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int row = 16 * ks + 8 * r + 4 * hlf + (jj >> 2);
+          const int off = row * HD + 8 * ((d >> 3) ^ swz_v<CPR>(row)) + (d & 7);
+          part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sv + off));
+        }
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
           o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][ks], o[db][qb], 0, 0, 0);
       }
+    }
+
+    if (have_next) {
+      // The other buffer was last read in iteration t-1; every wave has passed
+      // the barrier that ended it.
+      const int mk = store_tile(buf ^ 1);
+      tile_masked = GATHER ? __syncthreads_or(mk) : (__syncthreads(), 0);
     }
   }
 
   // ---- epilogue: O / l, lse = (m + log2 l) * ln 2
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    const float lt = pair_sum(l[qb]);
     const bool empty = (m[qb] == neg_inf());
     const float inv = empty ? 0.f : 1.f / lt;
     const float lse_v = empty ? neg_inf() : (m[qb] + log2f(lt)) * LN2;
@@ -346,52 +401,50 @@ void fwd_kernel(FwdParams p) {
 }
 
 struct Shape {
-  int qw, kt;
+  int qw, kt, waves, wpe;
 };
 
-// 64 rows per wave (256 per workgroup) halves the LDS operand traffic per MFMA
-// against 32 rows; groups of at most 128 rows (decode, one token's heads) use
-// 32 so no wave idles.  The key tile keeps S^T + P^T + O^T + Q^T within the
-// 512 registers a wave has at one wave per SIMD.
-Shape pick_shape(int hd, int rows_per_group) {
-  if (hd == 256) return {32, 64};
-  if (rows_per_group > 128) return {64, hd == 128 ? 64 : 128};
-  return {32, 128};
+// 32 rows per wave and 64-key tiles keep a wave within 256 registers at hd <=
+// 128, so two workgroups (8 waves) share a CU and overlap each other's softmax
+// and MFMA phases.  hd 256 needs the whole register file: one wave per SIMD.
+Shape pick_shape(int hd) {
+  if (hd == 256) return {32, 32, 4, 1};
+  return {32, 64, 4, 2};
 }
 
-template <int HD, int QW, int KT>
+template <int HD, int QW, int KT, int WAVES, int WPE>
 hipError_t launch_t(const FwdParams& p, bool gather, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles_per_group * p.n_groups * p.num_splits));
   if (gather)
-    hipLaunchKernelGGL((fwd_kernel<HD, QW, KT, true>), grid, dim3(THREADS), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<HD, QW, KT, WAVES, true, WPE>), grid, dim3(WAVES * 64), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<HD, QW, KT, false>), grid, dim3(THREADS), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<HD, QW, KT, WAVES, false, WPE>), grid, dim3(WAVES * 64), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int64_t fwd_grid_size(const FwdParams& p, int hd) {
-  const Shape sh = pick_shape(hd, p.rows_per_group);
-  const int64_t m_wg = (int64_t)WAVES * sh.qw;
+  const Shape sh = pick_shape(hd);
+  const int64_t m_wg = (int64_t)sh.waves * sh.qw;
   const int64_t tiles = (p.rows_per_group + m_wg - 1) / m_wg;
   return tiles * p.n_groups * p.num_splits;
 }
 
 hipError_t launch_fwd(FwdParams p, int hd, hipStream_t stream) {
-  const Shape sh = pick_shape(hd, p.rows_per_group);
-  const int m_wg = WAVES * sh.qw;
+  const Shape sh = pick_shape(hd);
+  const int m_wg = sh.waves * sh.qw;
   p.tiles_per_group = (p.rows_per_group + m_wg - 1) / m_wg;
   const bool gather = p.kv_idx != nullptr;
   switch (hd) {
     case 64:
-      return sh.qw == 64 ? launch_t<64, 64, 128>(p, gather, stream)
-                         : launch_t<64, 32, 128>(p, gather, stream);
+      return launch_t<64, 32, 64, 4, 2>(p, gather, stream);
     case 128:
-      return sh.qw == 64 ? launch_t<128, 64, 64>(p, gather, stream)
-                         : launch_t<128, 32, 128>(p, gather, stream);
+      return launch_t<128, 32, 64, 4, 2>(p, gather, stream);
     case 256:
-      return launch_t<256, 32, 64>(p, gather, stream);
+      return launch_t<256, 32, 32, 4, 1>(p, gather, stream);
     default:
       return hipErrorInvalidValue;
   }
