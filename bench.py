@@ -11,8 +11,8 @@ seeded synthetic input already resident in HBM:
   * sparse_topk  B=4 T=512 n_h=128 hd=128, 1024 of 32768 pool rows gathered per
     token (bf16 out) — TFLOP/s and gathered GB/s.
 Each call is timed with its own pair of HIP events on the launch stream, with
-L2 and the memory-side cache flushed (a 512 MiB write) before every timed call,
-so every call reads its inputs from HBM.  Back-to-back ("warm") times are
+L2 and the memory-side cache flushed (a read-only sweep of 512 MiB) before every
+timed call, so every call reads its inputs from HBM.  Back-to-back ("warm") times are
 reported beside them.  Rank 0 prints one JSON line.
 """
 from __future__ import annotations
@@ -105,7 +105,10 @@ def time_case(case, steps, warmup, flush_buf):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
-        flush_buf.fill_(i & 0xFF)
+        # read-only sweep: evicts L2/MALL (and writes back the previous call's
+        # dirty output) before the timed call instead of leaving dirty lines
+        # that drain inside it
+        flush_buf.sum()
         starts[i].record()
         case()
         ends[i].record()
@@ -265,7 +268,7 @@ def main():
     if args.only:
         profile_mode(args, dev)
         return
-    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush_buf = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
 
     res = {}
     for name, cid in CASES:

@@ -62,38 +62,24 @@ constexpr float RESCALE_THRESHOLD = 8.0f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
-// Swizzle of the 16-byte chunk index for K rows (A operand of S^T read with
-// ds_read_b128: 16 consecutive rows at one logical chunk must hit 16 distinct
-// bank groups; staging writes fill one row's chunks per 16 threads).
-template <int CPR>
-__device__ __forceinline__ int swz_k(int row) {
-  if constexpr (CPR >= 16) {
-    return (row ^ (row >> 3)) & 15;
-  } else {
-    return (row & 7) ^ ((row >> 3) & 1);
-  }
-}
+// LDS row strides (bytes).  K rows are read as ds_read_b128 by 16 lanes at 16
+// consecutive rows and one column: a 16-byte pad puts those rows on 16
+// distinct bank groups.  V rows are read by ds_read_b64_tr_b16, where the 32
+// lanes of a wave half read 4 consecutive rows x 64 bytes: a 64-byte pad puts
+// the 4 rows on disjoint bank ranges.  Padding (not an XOR swizzle) keeps every
+// operand address a per-lane base plus a compile-time offset.
+template <int HD>
+struct Lds {
+  static constexpr int K_STRIDE = HD * 2 + 16;
+  static constexpr int V_STRIDE = HD * 2 + 64;
+};
 
-// Swizzle for V rows, read by ds_read_b64_tr_b16: a 16-lane group reads 4
-// consecutive rows x 32 bytes (two chunks); the two groups of a wave half read
-// the neighbouring 32 bytes of the same rows.  The XOR values put the 4 rows'
-// chunk pairs (and quads) on distinct banks.
-template <int CPR>
-__device__ __forceinline__ int swz_v(int row) {
-  if constexpr (CPR >= 16) {
-    constexpr int f[4] = {0, 6, 10, 12};
-    return f[row & 3];
-  } else {
-    constexpr int f[4] = {0, 6, 4, 2};
-    return f[row & 3];
-  }
-}
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
+// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a;  // round to nearest even (v_cvt_pk_bf16_f32)
-  __bf16 y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float* s) {
@@ -136,11 +122,15 @@ void fwd_kernel(FwdParams p) {
   constexpr int TILE_CH = KT * CPR;            // chunks per K (or V) tile
   constexpr int CPT = TILE_CH / THREADS;       // chunks per thread per tile
   constexpr int ROWS_PER_PASS = THREADS / CPR;
+  constexpr int KS = Lds<HD>::K_STRIDE;
+  constexpr int VS = Lds<HD>::V_STRIDE;
+  constexpr int K_BYTES = KT * KS;
+  constexpr int V_BYTES = KT * VS;
   static_assert(QW % 32 == 0 && KT % 32 == 0 && HD % 32 == 0, "tile shape");
   static_assert(TILE_CH % THREADS == 0 && THREADS % CPR == 0, "staging shape");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][KT * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][KT * HD];
+  // [buf][K tile | V tile], padded rows
+  __shared__ __attribute__((aligned(16))) char smem[2][K_BYTES + V_BYTES];
   __shared__ int sValid[GATHER ? 2 : 1][KT];
 
   const int tid = threadIdx.x;
@@ -164,48 +154,72 @@ void fwd_kernel(FwdParams p) {
   const uint16_t* vbase = GATHER ? p.v : p.v + (int64_t)group * p.s_k * HD;
   const int32_t* ibase = GATHER ? p.kv_idx + (int64_t)group * p.s_k : nullptr;
 
-  // Staging assignment: chunk `sc` of rows srow0 + ROWS_PER_PASS*i.
+  // Staging assignment: chunk `sc` of tile rows srow0 + ROWS_PER_PASS*i.
   const int sc = tid % CPR;
   const int srow0 = tid / CPR;
 
-  // Global loads of one tile's K and V chunks into registers (zeros for keys
-  // outside [key_lo, key_hi) or with an out-of-range pool index).
+  // ---- staging: global -> registers -> LDS
   u32x4 rk[CPT], rv[CPT];
+  int ridx[CPT];   // gather: pool rows of the tile being loaded (-1 = masked)
   int rvalid[CPT];
-  auto load_tile = [&](int t) {
+  // Gather: pool-row indices of tile t (read one tile ahead of its K/V).
+  auto load_idx = [&](int t) {
     const int t0 = key_lo + t * KT;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int row = srow0 + ROWS_PER_PASS * i;
-      const int key = t0 + row;
-      int64_t off = (int64_t)key * HD;
-      bool ok = key < key_hi;
+      const int key = t0 + srow0 + ROWS_PER_PASS * i;
+      ridx[i] = key < key_hi ? ibase[key] : -1;
+    }
+  };
+  auto load_tile = [&](int t) {
+    const int t0 = key_lo + t * KT;
+    if (!GATHER && t0 + KT <= key_hi) {
+      // full dense tile: no predication
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int64_t off = (int64_t)(t0 + srow0 + ROWS_PER_PASS * i) * HD + 8 * sc;
+        rk[i] = *reinterpret_cast<const u32x4*>(kbase + off);
+        rv[i] = *reinterpret_cast<const u32x4*>(vbase + off);
+        rvalid[i] = 1;
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int key = t0 + srow0 + ROWS_PER_PASS * i;
+      int64_t row;
+      bool ok;
       if constexpr (GATHER) {
-        const int idx = ok ? ibase[key] : -1;
-        ok = ok && idx >= 0 && idx < p.pool_rows;
-        off = (int64_t)idx * HD;
+        const int idx = ridx[i];
+        ok = idx >= 0 && idx < p.pool_rows;
+        row = idx;
+      } else {
+        ok = key < key_hi;
+        row = key;
       }
       rvalid[i] = ok;
       rk[i] = u32x4{0u, 0u, 0u, 0u};
       rv[i] = u32x4{0u, 0u, 0u, 0u};
       if (ok) {
-        rk[i] = *reinterpret_cast<const u32x4*>(kbase + off + 8 * sc);
-        rv[i] = *reinterpret_cast<const u32x4*>(vbase + off + 8 * sc);
+        rk[i] = *reinterpret_cast<const u32x4*>(kbase + row * HD + 8 * sc);
+        rv[i] = *reinterpret_cast<const u32x4*>(vbase + row * HD + 8 * sc);
       }
     }
   };
-  // Returns nonzero when this thread saw a masked key (gather only).
+  // Returns nonzero when this thread staged a masked key (gather only).
   auto store_tile = [&](int buf) {
     int masked = 0;
+    char* sk = smem[buf];
+    char* sv = smem[buf] + K_BYTES;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int row = srow0 + ROWS_PER_PASS * i;
-      *reinterpret_cast<u32x4*>(&sK[buf][row * HD + 8 * (sc ^ swz_k<CPR>(row))]) = rk[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][row * HD + 8 * (sc ^ swz_v<CPR>(row))]) = rv[i];
+      *reinterpret_cast<u32x4*>(sk + row * KS + 16 * sc) = rk[i];
+      *reinterpret_cast<u32x4*>(sv + row * VS + 16 * sc) = rv[i];
       if constexpr (GATHER) {
         if (sc == 0) sValid[buf][row] = rvalid[i];
+        masked |= !rvalid[i];
       }
-      masked |= !rvalid[i];
     }
     return masked;
   };
@@ -241,15 +255,25 @@ void fwd_kernel(FwdParams p) {
   }
   const float c = p.scale_log2;
 
-  // V operand read offsets (bytes within a tile) for ds_read_b64_tr_b16: lane
-  // (jj = lane%16, dsub = lane/16%2, hlf) of K-step ks, d block db, half r reads
-  // row 16*ks + 8*r + 4*hlf + jj/4, columns d0 + 4*(jj%4) .. +3, d0 = 32*db + 16*dsub.
+  // Per-lane LDS byte offsets of the MFMA operands within a stage buffer.
+  //  K (A of S^T, ds_read_b128): row 32*kb + l32, bytes 32*ds + 16*hlf.
+  //  V (A of O^T, ds_read_b64_tr_b16): lane (jj, dsub, hlf) of K-step ks,
+  //  d block db and half r reads row 16*ks + 8*r + 4*hlf + jj/4, columns
+  //  32*db + 16*dsub + 4*(jj%4) .. +3; the 16-lane transpose then hands lane
+  //  (d = 32*db + lane%32, hlf) the keys 16*ks + 8*(e/4) + 4*hlf + e%4, e = 0..7,
+  //  which is where S^T's accumulator layout put that lane's P values.
   const int jj = lane & 15;
   const int dsub = (lane >> 4) & 1;
+  const int k_lane = l32 * KS + 16 * hlf;
+  const int v_lane = K_BYTES + (4 * hlf + (jj >> 2)) * VS + 2 * (16 * dsub + 4 * (jj & 3));
 
   int tile_masked = 0;
   if (n_tiles > 0) {
+    if constexpr (GATHER) load_idx(0);
     load_tile(0);
+    if constexpr (GATHER) {
+      if (n_tiles > 1) load_idx(1);
+    }
     const int mk = store_tile(0);
     tile_masked = GATHER ? __syncthreads_or(mk) : (__syncthreads(), 0);
   }
@@ -258,10 +282,13 @@ void fwd_kernel(FwdParams p) {
     const int buf = t & 1;
     const int t0 = key_lo + t * KT;
     const bool have_next = t + 1 < n_tiles;
-    if (have_next) load_tile(t + 1);
-
-    const uint16_t* sk = sK[buf];
-    const uint16_t* sv = sV[buf];
+    if (have_next) {
+      load_tile(t + 1);
+      if constexpr (GATHER) {
+        if (t + 2 < n_tiles) load_idx(t + 2);
+      }
+    }
+    const char* sb = smem[buf];
 
     // ---- S^T = K . Q^T  (unscaled dot products, fp32)
     f32x16 s[NKB][NQB];
@@ -275,10 +302,8 @@ void fwd_kernel(FwdParams p) {
     for (int ds = 0; ds < NDS; ++ds) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const int row = 32 * kb + l32;
-        const int ch = 2 * ds + hlf;
         const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(sk + row * HD + 8 * (ch ^ swz_k<CPR>(row)));
+            *reinterpret_cast<const bf16x8*>(sb + k_lane + kb * 32 * KS + ds * 32);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
           s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ds], s[kb][qb], 0, 0, 0);
@@ -342,14 +367,11 @@ void fwd_kernel(FwdParams p) {
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int d = 32 * db + 16 * dsub + 4 * (jj & 3);
         i16x4 part[2];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int row = 16 * ks + 8 * r + 4 * hlf + (jj >> 2);
-          const int off = row * HD + 8 * ((d >> 3) ^ swz_v<CPR>(row)) + (d & 7);
-          part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sv + off));
-        }
+        for (int r = 0; r < 2; ++r)
+          part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(sb + v_lane + (16 * ks + 8 * r) * VS + 64 * db));
         const bf16x8 a = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
