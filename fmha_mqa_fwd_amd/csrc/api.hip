@@ -64,7 +64,10 @@ int fmha_mqa_fwd(const void* q, const void* k, const void* v, const int32_t* kv_
   if (s_k > 0) {
     if (!k || !v) return FMHA_ERR_INVALID_ARG;
     if (gather && pool_rows < 1) return FMHA_ERR_INVALID_ARG;
-    if ((int64_t)B * T * s_k > INT64_MAX / 4) return FMHA_ERR_UNSUPPORTED;
+    // K/V rows are addressed with 32-bit byte offsets per batch (dense) or
+    // per pool (gather)
+    const int64_t kv_rows = gather ? (int64_t)pool_rows : (int64_t)s_k;
+    if (kv_rows * hd * 2 > INT32_MAX) return FMHA_ERR_UNSUPPORTED;
   }
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4)) return FMHA_ERR_ALIGNMENT;
   if (s_k > 0 && (!aligned(k, 16) || !aligned(v, 16))) return FMHA_ERR_ALIGNMENT;

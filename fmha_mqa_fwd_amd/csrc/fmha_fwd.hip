@@ -158,10 +158,15 @@ void fwd_kernel(FwdParams p) {
   const int sc = tid % CPR;
   const int srow0 = tid / CPR;
 
-  // ---- staging: global -> registers -> LDS
+  // ---- staging: global -> registers -> LDS, through buffer loads.  A buffer
+  // load whose offset lies beyond the descriptor's byte count returns zeros,
+  // which is how keys past the end of this split (dense) or with an
+  // out-of-range pool row (gather) become zero rows without predication.
   u32x4 rk[CPT], rv[CPT];
   int ridx[CPT];   // gather: pool rows of the tile being loaded (-1 = masked)
   int rvalid[CPT];
+  constexpr uint32_t ROW_BYTES = HD * 2;
+  constexpr uint32_t OOB = 0x80000000u;  // beyond any descriptor's byte count
   // Gather: pool-row indices of tile t (read one tile ahead of its K/V).
   auto load_idx = [&](int t) {
     const int t0 = key_lo + t * KT;
@@ -173,36 +178,33 @@ void fwd_kernel(FwdParams p) {
   };
   auto load_tile = [&](int t) {
     const int t0 = key_lo + t * KT;
-    if (!GATHER && t0 + KT <= key_hi) {
-      // full dense tile: no predication
+    if constexpr (GATHER) {
+      const auto rsk = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)p.k, (short)0, (int)((uint32_t)p.pool_rows * ROW_BYTES), 0x00020000);
+      const auto rsv = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)p.v, (short)0, (int)((uint32_t)p.pool_rows * ROW_BYTES), 0x00020000);
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int64_t off = (int64_t)(t0 + srow0 + ROWS_PER_PASS * i) * HD + 8 * sc;
-        rk[i] = *reinterpret_cast<const u32x4*>(kbase + off);
-        rv[i] = *reinterpret_cast<const u32x4*>(vbase + off);
-        rvalid[i] = 1;
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int key = t0 + srow0 + ROWS_PER_PASS * i;
-      int64_t row;
-      bool ok;
-      if constexpr (GATHER) {
         const int idx = ridx[i];
-        ok = idx >= 0 && idx < p.pool_rows;
-        row = idx;
-      } else {
-        ok = key < key_hi;
-        row = key;
+        const bool ok = idx >= 0 && idx < p.pool_rows;
+        rvalid[i] = ok;
+        const uint32_t off = ok ? (uint32_t)idx * ROW_BYTES + 16 * sc : OOB;
+        rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsk, off, 0, 0));
+        rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsv, off, 0, 0));
       }
-      rvalid[i] = ok;
-      rk[i] = u32x4{0u, 0u, 0u, 0u};
-      rv[i] = u32x4{0u, 0u, 0u, 0u};
-      if (ok) {
-        rk[i] = *reinterpret_cast<const u32x4*>(kbase + row * HD + 8 * sc);
-        rv[i] = *reinterpret_cast<const u32x4*>(vbase + row * HD + 8 * sc);
+    } else {
+      // descriptor covers keys t0 .. key_hi-1 of this group
+      const int nbytes = (key_hi - t0) * (int)ROW_BYTES;
+      const auto rsk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)t0 * HD),
+                                                         (short)0, nbytes, 0x00020000);
+      const auto rsv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)t0 * HD),
+                                                         (short)0, nbytes, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const uint32_t off = (uint32_t)(srow0 + ROWS_PER_PASS * i) * ROW_BYTES + 16 * sc;
+        rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsk, off, 0, 0));
+        rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsv, off, 0, 0));
+        rvalid[i] = 1;
       }
     }
   };
@@ -426,47 +428,48 @@ struct Shape {
   int qw, kt, waves, wpe;
 };
 
-// 32 rows per wave and 64-key tiles keep a wave within 256 registers at hd <=
-// 128, so two workgroups (8 waves) share a CU and overlap each other's softmax
-// and MFMA phases.  hd 256 needs the whole register file: one wave per SIMD.
-Shape pick_shape(int hd) {
+// 32 rows per wave keeps a wave within 170 (dense, 32-key tiles: three waves
+// per SIMD) or 256 (gather, 64-key tiles: two waves per SIMD) registers, so
+// one wave's softmax overlaps other waves' MFMAs.  hd 256 needs the whole
+// register file: one wave per SIMD.
+Shape pick_shape(int hd, bool gather) {
   if (hd == 256) return {32, 32, 4, 1};
-  return {32, 64, 4, 2};
+  if (gather) return {32, 64, 4, 2};
+  return {32, 32, 4, 3};
 }
 
-template <int HD, int QW, int KT, int WAVES, int WPE>
-hipError_t launch_t(const FwdParams& p, bool gather, hipStream_t stream) {
+template <int HD, int QW, int KT, int WAVES, int WPE, bool GATHER>
+hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles_per_group * p.n_groups * p.num_splits));
-  if (gather)
-    hipLaunchKernelGGL((fwd_kernel<HD, QW, KT, WAVES, true, WPE>), grid, dim3(WAVES * 64), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((fwd_kernel<HD, QW, KT, WAVES, false, WPE>), grid, dim3(WAVES * 64), 0,
-                       stream, p);
+  hipLaunchKernelGGL((fwd_kernel<HD, QW, KT, WAVES, GATHER, WPE>), grid, dim3(WAVES * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int64_t fwd_grid_size(const FwdParams& p, int hd) {
-  const Shape sh = pick_shape(hd);
+  const Shape sh = pick_shape(hd, p.kv_idx != nullptr);
   const int64_t m_wg = (int64_t)sh.waves * sh.qw;
   const int64_t tiles = (p.rows_per_group + m_wg - 1) / m_wg;
   return tiles * p.n_groups * p.num_splits;
 }
 
 hipError_t launch_fwd(FwdParams p, int hd, hipStream_t stream) {
-  const Shape sh = pick_shape(hd);
+  const bool gather = p.kv_idx != nullptr;
+  const Shape sh = pick_shape(hd, gather);
   const int m_wg = sh.waves * sh.qw;
   p.tiles_per_group = (p.rows_per_group + m_wg - 1) / m_wg;
-  const bool gather = p.kv_idx != nullptr;
   switch (hd) {
     case 64:
-      return launch_t<64, 32, 64, 4, 2>(p, gather, stream);
+      return gather ? launch_t<64, 32, 64, 4, 2, true>(p, stream)
+                    : launch_t<64, 32, 32, 4, 3, false>(p, stream);
     case 128:
-      return launch_t<128, 32, 64, 4, 2>(p, gather, stream);
+      return gather ? launch_t<128, 32, 64, 4, 2, true>(p, stream)
+                    : launch_t<128, 32, 32, 4, 3, false>(p, stream);
     case 256:
-      return launch_t<256, 32, 32, 4, 1>(p, gather, stream);
+      return gather ? launch_t<256, 32, 32, 4, 1, true>(p, stream)
+                    : launch_t<256, 32, 32, 4, 1, false>(p, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -47,7 +47,8 @@ extern "C" {
 typedef enum {
   FMHA_OK = 0,
   FMHA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad dtype/scale/splits */
-  FMHA_ERR_UNSUPPORTED = 2, /* head dim not in {64, 128, 256}; sizes beyond int32 rows */
+  FMHA_ERR_UNSUPPORTED = 2, /* head dim not in {64, 128, 256}; more than 2^31-1 rows;
+                               K/V (s_k rows dense, pool_rows gather) over 2 GiB */
   FMHA_ERR_ALIGNMENT = 3,   /* a tensor pointer not 16-byte aligned (lse: 4-byte) */
   FMHA_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned */
   FMHA_ERR_LAUNCH = 5       /* the HIP runtime rejected a kernel launch */
