@@ -1,0 +1,321 @@
+// Device-side building blocks shared by the attention kernels (gfx950).
+//
+// One 32x32x16 bf16 MFMA tile of S^T = K.Q^T holds, in lane l, query column
+// l%32 and the 16 keys 8*(r/4) + 4*(l/32) + r%4 (r = accumulator register).
+// Every row statistic is therefore in-lane plus one exchange with lane l^32,
+// and the bf16-rounded accumulators are, register for register, the B operand
+// of the PV MFMA O^T = V^T.P^T when V's A operand lists the keys of each
+// 16-key step in the order 8*(e/4) + 4*(l/32) + e%4, e = 0..7.
+//
+// The steps follow the pages' pipeline (page "CURRENT ISSUE: UMMA FMHA — Full
+// Pipeline + Production", "What's working": QK -> softmax -> PV -> output;
+// "Key lessons from this session": the scale is applied in the softmax) and the
+// multi-KV-tile O rescale (page "May 24, 2026 — Session Start Plan", section 2).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fmha_internal.h"
+
+namespace fmha {
+namespace dev {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr float LN2 = 0.6931471805599453f;
+// The running max used for the exponentials moves only when a row's tile max
+// exceeds it by more than this (log2 units): exponentials then stay <= 2^8,
+// far inside fp32/bf16 range, and O/l need rescaling on few tiles.  Exact: O
+// and l always share the maximum they were computed against.
+constexpr float RESCALE_THRESHOLD = 8.0f;
+// gfx9 raw buffer descriptor word 3 (32-bit data, no swizzle, offset mode)
+constexpr int BUF_FLAGS = 0x00020000;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* s) {
+  u32x4 w;
+  w[0] = pack_bf16x2(s[0], s[1]);
+  w[1] = pack_bf16x2(s[2], s[3]);
+  w[2] = pack_bf16x2(s[4], s[5]);
+  w[3] = pack_bf16x2(s[6], s[7]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Value of lane l^32 combined with this lane's: max and sum across the halves.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Key (within a 32-key block) held by accumulator register r of a lane in half
+// `hlf` of the wave (32x32 MFMA output layout).
+__device__ __forceinline__ int acc_row(int r, int hlf) { return 8 * (r >> 2) + 4 * hlf + (r & 3); }
+
+// Per-wave state of QW query rows (NQB = QW/32 column blocks).
+template <int HD, int QW>
+struct Rows {
+  static constexpr int NQB = QW / 32;
+  static constexpr int NDS = HD / 16;  // 16-wide contraction steps of QK^T
+  static constexpr int NDB = HD / 32;  // 32-wide d blocks of O^T
+  bf16x8 qf[NQB][NDS];                 // Q^T fragments (B operand of S^T)
+  f32x16 o[NDB][NQB];                  // O^T accumulators
+  float m[NQB];                        // running max, scaled, log2 units
+  float l[NQB];                        // this lane-half's running row sum
+  float alpha[NQB];                    // last rescale factor
+
+  // Lane (hlf, l32) of block qb holds q[row l32][16*ds + 8*hlf .. +7].
+  __device__ __forceinline__ void load_q(const uint16_t* q, int64_t grow0, int row0,
+                                         int rows_in_group, int l32, int hlf) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int r = row0 + qb * 32 + l32;
+      const bool ok = r < rows_in_group;
+      const uint16_t* qrow = q + (grow0 + (ok ? r : 0)) * HD + 8 * hlf;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (ok) w = *reinterpret_cast<const u32x4*>(qrow + 16 * ds);
+        qf[qb][ds] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][qb][i] = 0.f;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      m[qb] = neg_inf();
+      l[qb] = 0.f;
+      alpha[qb] = 1.f;
+    }
+  }
+
+  // S^T[kb][qb] = K_tile . Q^T with kfrag(kb, ds) the 16-byte A fragment of
+  // key block kb (32 keys) and contraction step ds.
+  template <int NKB, class KFrag>
+  __device__ __forceinline__ void qk(f32x16 (&s)[NKB][NQB], KFrag kfrag) const {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 a = kfrag(kb, ds);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ds], s[kb][qb], 0, 0, 0);
+      }
+    }
+  }
+
+  // -inf for the keys of this tile for which key_ok(key within tile) is false.
+  template <int NKB, class KeyOk>
+  __device__ __forceinline__ void mask(f32x16 (&s)[NKB][NQB], int hlf, KeyOk key_ok) const {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (!key_ok(32 * kb + acc_row(r, hlf))) {
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) s[kb][qb][r] = neg_inf();
+        }
+      }
+  }
+
+  // Online softmax of one tile in base 2 (x*scale*log2e - m in one FMA), with
+  // the lazy running max.  Writes the bf16 P^T fragments; returns whether some
+  // row's max moved (then O must be scaled by alpha before the next PV).
+  template <int NKB>
+  __device__ __forceinline__ int softmax(f32x16 (&s)[NKB][NQB], bf16x8 (&pf)[NQB][2 * NKB],
+                                         float c) {
+    int any = 0;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      float mx = neg_inf();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+      const float m_tile = pair_max(mx) * c;
+      const bool resc = __any(m_tile > m[qb] + RESCALE_THRESHOLD);
+      any |= resc;
+      const float m_new = resc ? fmaxf(m[qb], m_tile) : m[qb];
+      const float a = (m[qb] == neg_inf()) ? 0.f
+                      : (m_new == m[qb])   ? 1.f
+                                           : __builtin_amdgcn_exp2f(m[qb] - m_new);
+      alpha[qb] = a;
+      l[qb] *= a;
+      m[qb] = m_new;
+      const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float pv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pv[r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c, -m_use));
+          ls += pv[r];
+        }
+        pf[qb][2 * kb] = pack_bf16x8(pv);
+        pf[qb][2 * kb + 1] = pack_bf16x8(pv + 8);
+      }
+      l[qb] += ls;
+    }
+    return any;
+  }
+
+  __device__ __forceinline__ void rescale_o() {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][qb][i] *= alpha[qb];
+  }
+
+  // O^T += V^T . P^T with vfrag(ks, db) the A fragment of 16-key step ks and
+  // d block db (keys in the accumulator order described above).
+  template <int NKS, class VFrag>
+  __device__ __forceinline__ void pv(const bf16x8 (&pf)[NQB][NKS], VFrag vfrag) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 a = vfrag(ks, db);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][ks], o[db][qb], 0, 0, 0);
+      }
+    }
+  }
+
+  // O / l and lse = (m + log2 l) ln 2; an empty row (no key seen) gets O = 0,
+  // lse = -inf.  OUT_PARTIAL writes fp32 to plane `split` of [splits, rows, HD].
+  // Direct form: each lane stores its own 4-element pieces (a row's 32-wide d
+  // block arrives as 8 pieces from 2 lanes per instruction).
+  __device__ __forceinline__ void store(const FwdParams& p, int64_t grow0, int row0, int split,
+                                        int l32, int hlf) const {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const float lt = pair_sum(l[qb]);
+      const bool empty = (m[qb] == neg_inf());
+      const float inv = empty ? 0.f : 1.f / lt;
+      const float lse_v = empty ? neg_inf() : (m[qb] + log2f(lt)) * LN2;
+      const int r = row0 + qb * 32 + l32;
+      if (r >= p.rows_per_group) continue;
+      const int64_t row = grow0 + r;
+      const int64_t base = (p.out_mode == OUT_PARTIAL) ? (int64_t)split * p.total_rows : 0;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d = 32 * db + 8 * rg + 4 * hlf;
+          f32x4 val;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) val[i] = o[db][qb][4 * rg + i] * inv;
+          if (p.out_mode == OUT_BF16) {
+            u32x2 w = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row * HD + d) = w;
+          } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + (base + row) * HD + d) = val;
+          }
+        }
+      }
+      if (hlf == 0) p.lse[base + row] = lse_v;
+    }
+  }
+
+  // Same result, staged through LDS so that memory sees whole output rows:
+  // the wave writes its 32 rows (per column block) into LDS, 16-byte chunks
+  // XOR-swizzled by row, then consecutive lanes store consecutive 16-byte
+  // chunks of each row.  row_addr(r) is the LDS byte address of local row r
+  // (0..31), holding at least HD*4 bytes; only this wave touches it.
+  template <class RowAddr>
+  __device__ __forceinline__ void store_lds(const FwdParams& p, int64_t grow0, int row0, int split,
+                                            int lane, RowAddr row_addr) const {
+    const int l32 = lane & 31;
+    const int hlf = lane >> 5;
+    const bool bf = (p.out_mode == OUT_BF16);
+    const int rb = HD * (bf ? 2 : 4);   // output bytes per row
+    const int cpr = rb / 16;            // 16-byte chunks per row (8 .. 64)
+    const int swm = cpr >= 16 ? 15 : 7;
+    const int64_t base = (p.out_mode == OUT_PARTIAL) ? (int64_t)split * p.total_rows : 0;
+    char* const out = static_cast<char*>(p.out);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const float lt = pair_sum(l[qb]);
+      const bool empty = (m[qb] == neg_inf());
+      const float inv = empty ? 0.f : 1.f / lt;
+      const float lse_v = empty ? neg_inf() : (m[qb] + log2f(lt)) * LN2;
+      char* const my = row_addr(l32);
+      const int sw = l32 & swm;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d = 32 * db + 8 * rg + 4 * hlf;
+          f32x4 val;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) val[i] = o[db][qb][4 * rg + i] * inv;
+          if (bf) {
+            const u32x2 w = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+            *reinterpret_cast<u32x2*>(my + 16 * ((d >> 3) ^ sw) + 2 * (d & 7)) = w;
+          } else {
+            *reinterpret_cast<f32x4*>(my + 16 * ((d >> 2) ^ sw)) = val;
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int rpi = 64 / cpr;  // rows per store instruction
+      for (int r = lane / cpr; r < 32; r += rpi) {
+        const int ch = lane % cpr;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row_addr(r) + 16 * (ch ^ (r & swm)));
+        const int rr = row0 + qb * 32 + r;
+        if (rr < p.rows_per_group)
+          *reinterpret_cast<u32x4*>(out + (base + grow0 + rr) * rb + 16 * ch) = v;
+      }
+      const int r = row0 + qb * 32 + l32;
+      if (hlf == 0 && r < p.rows_per_group) p.lse[base + grow0 + r] = lse_v;
+      __builtin_amdgcn_wave_barrier();  // LDS reads done before the next block's writes
+    }
+  }
+};
+
+// A V fragment from two ds_read_b64_tr_b16 reads at byte addresses a0 (keys
+// e = 0..3) and a1 (keys e = 4..7) within LDS.
+__device__ __forceinline__ bf16x8 v_frag_tr(const char* a0, const char* a1) {
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
+  const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+}  // namespace dev
+}  // namespace fmha

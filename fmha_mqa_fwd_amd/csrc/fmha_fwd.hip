@@ -40,27 +40,14 @@
 //     allow, so one wave's softmax overlaps another's MFMAs.
 //   * LDS rows use XOR swizzles of 16-byte chunks chosen so that the MFMA operand
 //     reads and the staging writes are free of bank conflicts.
-#include <math.h>
+#include <type_traits>
 
-#include "fmha_internal.h"
+#include "fmha_device.h"
 
 namespace fmha {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-
-constexpr float LN2 = 0.6931471805599453f;
-// The running max moves only when a row max exceeds it by more than this
-// (log2 units): exponentials then stay <= 2^8, far inside fp32/bf16 range.
-constexpr float RESCALE_THRESHOLD = 8.0f;
-
-__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+using namespace dev;
 
 // LDS row strides (bytes).  K rows are read as ds_read_b128 by 16 lanes at 16
 // consecutive rows and one column: a 16-byte pad puts those rows on 16
@@ -74,49 +61,15 @@ struct Lds {
   static constexpr int V_STRIDE = HD * 2 + 64;
 };
 
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-
-// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-
-__device__ __forceinline__ bf16x8 pack_bf16x8(const float* s) {
-  u32x4 w;
-  w[0] = pack_bf16x2(s[0], s[1]);
-  w[1] = pack_bf16x2(s[2], s[3]);
-  w[2] = pack_bf16x2(s[4], s[5]);
-  w[3] = pack_bf16x2(s[6], s[7]);
-  return __builtin_bit_cast(bf16x8, w);
-}
-
-// Value of lane l^32 combined with this lane's: max and sum across the halves.
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Key (within a 32-key block) held by accumulator register r of a lane in
-// half `hlf`, for the 32x32 MFMA output layout: register r covers row
-// 8*(r/4) + 4*hlf + r%4 at column lane%32.
-__device__ __forceinline__ int acc_row(int r, int hlf) {
-  return 8 * (r >> 2) + 4 * hlf + (r & 3);
-}
-
+// Streaming kernel: a workgroup takes WAVES*QW rows of one group and walks the
+// keys of its split in KT-key tiles, double-buffered in LDS.
 template <int HD, int QW, int KT, int WAVES, bool GATHER, int WPE>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(FwdParams p) {
   constexpr int THREADS = WAVES * 64;
-  constexpr int NQB = QW / 32;   // 32-query MFMA column blocks per wave
-  constexpr int NDS = HD / 16;   // 16-wide contraction steps of QK^T
+  constexpr int NQB = QW / 32;
   constexpr int NKB = KT / 32;   // 32-key row blocks of S^T per tile
   constexpr int NKS = KT / 16;   // 16-key contraction steps of PV per tile
-  constexpr int NDB = HD / 32;   // 32-wide d blocks of O^T
   constexpr int CPR = HD / 8;    // 16-byte chunks per K/V row
   constexpr int M_WG = WAVES * QW;
   constexpr int TILE_CH = KT * CPR;            // chunks per K (or V) tile
@@ -180,9 +133,9 @@ void fwd_kernel(FwdParams p) {
     const int t0 = key_lo + t * KT;
     if constexpr (GATHER) {
       const auto rsk = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)p.k, (short)0, (int)((uint32_t)p.pool_rows * ROW_BYTES), 0x00020000);
+          (void*)p.k, (short)0, (int)((uint32_t)p.pool_rows * ROW_BYTES), BUF_FLAGS);
       const auto rsv = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)p.v, (short)0, (int)((uint32_t)p.pool_rows * ROW_BYTES), 0x00020000);
+          (void*)p.v, (short)0, (int)((uint32_t)p.pool_rows * ROW_BYTES), BUF_FLAGS);
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const int idx = ridx[i];
@@ -196,9 +149,9 @@ void fwd_kernel(FwdParams p) {
       // descriptor covers keys t0 .. key_hi-1 of this group
       const int nbytes = (key_hi - t0) * (int)ROW_BYTES;
       const auto rsk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)t0 * HD),
-                                                         (short)0, nbytes, 0x00020000);
+                                                         (short)0, nbytes, BUF_FLAGS);
       const auto rsv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)t0 * HD),
-                                                         (short)0, nbytes, 0x00020000);
+                                                         (short)0, nbytes, BUF_FLAGS);
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const uint32_t off = (uint32_t)(srow0 + ROWS_PER_PASS * i) * ROW_BYTES + 16 * sc;
@@ -226,35 +179,8 @@ void fwd_kernel(FwdParams p) {
     return masked;
   };
 
-  // Q^T fragments (B operand of S^T = K.Q^T): lane (hlf, l32) of column block
-  // qb holds q[row l32][16*ds + 8*hlf .. +7] for every contraction step ds.
-  bf16x8 qf[NQB][NDS];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int r = row0 + qb * 32 + l32;
-    const bool ok = r < p.rows_per_group;
-    const uint16_t* qrow = p.q + (grow0 + (ok ? r : 0)) * HD + 8 * hlf;
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (ok) w = *reinterpret_cast<const u32x4*>(qrow + 16 * ds);
-      qf[qb][ds] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
-
-  f32x16 o[NDB][NQB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][qb][i] = 0.f;
-  float m[NQB], l[NQB];  // running max (scaled, log2 units) and partial row sum
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    m[qb] = neg_inf();
-    l[qb] = 0.f;
-  }
+  Rows<HD, QW> w;
+  w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf);
   const float c = p.scale_log2;
 
   // Per-lane LDS byte offsets of the MFMA operands within a stage buffer.
@@ -292,95 +218,21 @@ void fwd_kernel(FwdParams p) {
     }
     const char* sb = smem[buf];
 
-    // ---- S^T = K . Q^T  (unscaled dot products, fp32)
     f32x16 s[NKB][NQB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.f;
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(sb + k_lane + kb * 32 * KS + ds * 32);
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ds], s[kb][qb], 0, 0, 0);
-      }
+    w.template qk<NKB>(s, [&](int kb, int ds) {
+      return *reinterpret_cast<const bf16x8*>(sb + k_lane + kb * 32 * KS + ds * 32);
+    });
+    if ((!GATHER && t0 + KT > key_hi) || (GATHER && tile_masked)) {
+      w.template mask<NKB>(s, hlf, [&](int kr) {
+        return GATHER ? (sValid[buf][kr] != 0) : (t0 + kr < key_hi);
+      });
     }
-    const bool dense_tail = !GATHER && (t0 + KT > key_hi);
-    if (dense_tail || (GATHER && tile_masked)) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kr = 32 * kb + acc_row(r, hlf);
-          const bool ok = GATHER ? (sValid[buf][kr] != 0) : (t0 + kr < key_hi);
-          if (!ok) {
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) s[kb][qb][r] = neg_inf();
-          }
-        }
-    }
-
-    // ---- online softmax (base 2) with lazy rescale
     bf16x8 pf[NQB][NKS];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      float mx = neg_inf();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      const float m_tile = pair_max(mx) * c;
-      if (__any(m_tile > m[qb] + RESCALE_THRESHOLD)) {
-        const float m_new = fmaxf(m[qb], m_tile);
-        const float m_old_use = (m[qb] == neg_inf()) ? m_new : m[qb];
-        const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(m_old_use - m_new);
-        const float a0 = (m[qb] == neg_inf()) ? 0.f : alpha;
-        l[qb] *= a0;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][qb][i] *= a0;
-        m[qb] = m_new;
-      }
-      const float m_use = (m[qb] == neg_inf()) ? 0.f : m[qb];
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        float pv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pv[r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c, -m_use));
-          ls += pv[r];
-        }
-        pf[qb][2 * kb] = pack_bf16x8(pv);
-        pf[qb][2 * kb + 1] = pack_bf16x8(pv + 8);
-      }
-      l[qb] += ls;
-    }
-
-    // ---- O^T += V^T . P^T
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        i16x4 part[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-          part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(sb + v_lane + (16 * ks + 8 * r) * VS + 64 * db));
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][ks], o[db][qb], 0, 0, 0);
-      }
-    }
+    if (w.template softmax<NKB>(s, pf, c)) w.rescale_o();
+    w.template pv<NKS>(pf, [&](int ks, int db) {
+      const char* a = sb + v_lane + 16 * ks * VS + 64 * db;
+      return v_frag_tr(a, a + 8 * VS);
+    });
 
     if (have_next) {
       // The other buffer was last read in iteration t-1; every wave has passed
@@ -389,39 +241,19 @@ void fwd_kernel(FwdParams p) {
       tile_masked = GATHER ? __syncthreads_or(mk) : (__syncthreads(), 0);
     }
   }
-
-  // ---- epilogue: O / l, lse = (m + log2 l) * ln 2
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const float lt = pair_sum(l[qb]);
-    const bool empty = (m[qb] == neg_inf());
-    const float inv = empty ? 0.f : 1.f / lt;
-    const float lse_v = empty ? neg_inf() : (m[qb] + log2f(lt)) * LN2;
-    const int r = row0 + qb * 32 + l32;
-    if (r >= p.rows_per_group) continue;
-    const int64_t row = grow0 + r;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d = 32 * db + 8 * rg + 4 * hlf;
-        f32x4 val;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) val[i] = o[db][qb][4 * rg + i] * inv;
-        if (p.out_mode == OUT_BF16) {
-          u32x2 w = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row * HD + d) = w;
-        } else {
-          const int64_t base = (p.out_mode == OUT_PARTIAL) ? (int64_t)split * p.total_rows : 0;
-          *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + (base + row) * HD + d) = val;
-        }
-      }
-    }
-    if (hlf == 0) {
-      const int64_t base = (p.out_mode == OUT_PARTIAL) ? (int64_t)split * p.total_rows : 0;
-      p.lse[base + row] = lse_v;
+  // Epilogue through LDS when this workgroup's output rows fit in the stage
+  // buffers (bf16 at hd <= 128), else each lane stores its own pieces.
+  constexpr int SMEM_BYTES = 2 * (K_BYTES + V_BYTES);
+  constexpr int RB_BF16 = HD * 2;
+  if constexpr (WAVES * QW * RB_BF16 <= SMEM_BYTES) {
+    if (p.out_mode == OUT_BF16) {
+      __syncthreads();
+      char* const region = &smem[0][0] + wave * QW * RB_BF16;
+      w.store_lds(p, grow0, row0, split, lane, [&](int r) { return region + r * RB_BF16; });
+      return;
     }
   }
+  w.store(p, grow0, row0, split, l32, hlf);
 }
 
 struct Shape {
@@ -450,12 +282,14 @@ hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
 
 int64_t fwd_grid_size(const FwdParams& p, int hd) {
   const Shape sh = pick_shape(hd, p.kv_idx != nullptr);
-  const int64_t m_wg = (int64_t)sh.waves * sh.qw;
+  const int64_t m_wg = (p.chunk <= chunk_max_keys(hd)) ? 128 : (int64_t)sh.waves * sh.qw;
   const int64_t tiles = (p.rows_per_group + m_wg - 1) / m_wg;
   return tiles * p.n_groups * p.num_splits;
 }
 
 hipError_t launch_fwd(FwdParams p, int hd, hipStream_t stream) {
+  // a split that fits in LDS whole is staged at once (decode shapes)
+  if (p.chunk <= chunk_max_keys(hd)) return launch_chunk(p, hd, stream);
   const bool gather = p.kv_idx != nullptr;
   const Shape sh = pick_shape(hd, gather);
   const int m_wg = sh.waves * sh.qw;

@@ -39,6 +39,11 @@ hipError_t launch_fwd(FwdParams p, int hd, hipStream_t stream);
 // Number of workgroups launch_fwd would start (for the host-side size check).
 int64_t fwd_grid_size(const FwdParams& p, int hd);
 
+// Whole-chunk variant: valid when one split's keys (p.chunk) number at most
+// chunk_max_keys(hd); stages them in LDS at once.  Sets p.tiles_per_group.
+int chunk_max_keys(int hd);
+hipError_t launch_chunk(FwdParams p, int hd, hipStream_t stream);
+
 // out[r] = sum_i w_i o_i[r] / sum_i w_i with w_i = exp(lse_i[r] - max_i lse_i[r]).
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_parts,
                         int rows, int hd, void* out, bool out_bf16, float* lse,

@@ -9,28 +9,26 @@
 // The kernel is bound by HBM/L2 bandwidth: each thread owns one 16-byte chunk
 // (4 floats) of one output row, reads that chunk from every part with 16-byte
 // loads (consecutive threads -> consecutive chunks of a row, so every wave
-// reads whole contiguous segments) and writes it once.
+// reads whole contiguous segments) and writes it once.  For the usual part
+// counts all of a thread's loads are in flight together.
 #include <math.h>
 
-#include "fmha_internal.h"
+#include "fmha_device.h"
 
 namespace fmha {
 namespace {
 
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+using dev::f32x4;
+using dev::u32x2;
+using dev::pack_bf16x2;
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a;
-  __bf16 y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-}
-
-template <bool OUT_BF16>
+// NP > 0: the part count is a compile-time constant, so every lse and O load
+// of a thread is issued before any arithmetic (one memory round trip per
+// thread instead of one per part).  NP == 0: any count, loop over parts.
+template <bool OUT_BF16, int NP>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_parts,
                                                     const float* __restrict__ lse_parts,
                                                     int n_parts, int rows, int hd,
@@ -39,25 +37,48 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   const int cpr = hd >> 2;  // 16-byte chunks per row
   const int64_t total = (int64_t)rows * cpr;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int np = NP > 0 ? NP : n_parts;
   for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += stride) {
     const int row = (int)(u / cpr);
     const int ch = (int)(u % cpr);
-    float mx = -__builtin_inff();
-    for (int i = 0; i < n_parts; ++i) mx = fmaxf(mx, lse_parts[(int64_t)i * rows + row]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float mx = -__builtin_inff();
     float den = 0.f;
-    const bool live = mx != -__builtin_inff();
-    if (live) {
-      for (int i = 0; i < n_parts; ++i) {
-        const float li = lse_parts[(int64_t)i * rows + row];
-        if (li == -__builtin_inff()) continue;  // empty part: its o_i is never read
-        const float w = __builtin_amdgcn_exp2f((li - mx) * LOG2E);
-        den += w;
-        const f32x4 oi =
-            *reinterpret_cast<const f32x4*>(o_parts + ((int64_t)i * rows + row) * hd + 4 * ch);
-        acc += w * oi;
+    if constexpr (NP > 0) {
+      float li[NP];
+      f32x4 oi[NP];
+#pragma unroll
+      for (int i = 0; i < NP; ++i) li[i] = lse_parts[(int64_t)i * rows + row];
+#pragma unroll
+      for (int i = 0; i < NP; ++i)
+        oi[i] = *reinterpret_cast<const f32x4*>(o_parts + ((int64_t)i * rows + row) * hd + 4 * ch);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) mx = fmaxf(mx, li[i]);
+      if (mx != -__builtin_inff()) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          // an empty part (lse -inf) gets weight 0 and its O is not used
+          const bool live = li[i] != -__builtin_inff();
+          const float w = live ? __builtin_amdgcn_exp2f((li[i] - mx) * LOG2E) : 0.f;
+          den += w;
+          if (live) acc += w * oi[i];
+        }
+        acc *= 1.f / den;
       }
-      acc *= 1.f / den;
+    } else {
+      for (int i = 0; i < np; ++i) mx = fmaxf(mx, lse_parts[(int64_t)i * rows + row]);
+      if (mx != -__builtin_inff()) {
+        for (int i = 0; i < np; ++i) {
+          const float li = lse_parts[(int64_t)i * rows + row];
+          if (li == -__builtin_inff()) continue;  // empty part: its o_i is never read
+          const float w = __builtin_amdgcn_exp2f((li - mx) * LOG2E);
+          den += w;
+          const f32x4 oi =
+              *reinterpret_cast<const f32x4*>(o_parts + ((int64_t)i * rows + row) * hd + 4 * ch);
+          acc += w * oi;
+        }
+        acc *= 1.f / den;
+      }
     }
     if constexpr (OUT_BF16) {
       u32x2 w = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
@@ -65,8 +86,20 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
     } else {
       *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)row * hd + 4 * ch) = acc;
     }
-    if (ch == 0 && lse != nullptr) lse[row] = live ? mx + log2f(den) * LN2 : -__builtin_inff();
+    if (ch == 0 && lse != nullptr)
+      lse[row] = (mx != -__builtin_inff()) ? mx + log2f(den) * LN2 : -__builtin_inff();
   }
+}
+
+template <int NP>
+void launch_np(bool out_bf16, dim3 grid, hipStream_t stream, const float* o_parts,
+               const float* lse_parts, int n_parts, int rows, int hd, void* out, float* lse) {
+  if (out_bf16)
+    hipLaunchKernelGGL((merge_kernel<true, NP>), grid, dim3(256), 0, stream, o_parts, lse_parts,
+                       n_parts, rows, hd, out, lse);
+  else
+    hipLaunchKernelGGL((merge_kernel<false, NP>), grid, dim3(256), 0, stream, o_parts, lse_parts,
+                       n_parts, rows, hd, out, lse);
 }
 
 }  // namespace
@@ -77,12 +110,19 @@ hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_part
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  if (out_bf16)
-    hipLaunchKernelGGL(merge_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, o_parts,
-                       lse_parts, n_parts, rows, hd, out, lse);
-  else
-    hipLaunchKernelGGL(merge_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, o_parts,
-                       lse_parts, n_parts, rows, hd, out, lse);
+  const dim3 grid((unsigned)blocks);
+  switch (n_parts) {
+#define FMHA_MERGE_CASE(N) \
+  case N:                  \
+    launch_np<N>(out_bf16, grid, stream, o_parts, lse_parts, n_parts, rows, hd, out, lse); \
+    break;
+    FMHA_MERGE_CASE(1) FMHA_MERGE_CASE(2) FMHA_MERGE_CASE(3) FMHA_MERGE_CASE(4)
+    FMHA_MERGE_CASE(5) FMHA_MERGE_CASE(6) FMHA_MERGE_CASE(7) FMHA_MERGE_CASE(8)
+    FMHA_MERGE_CASE(12) FMHA_MERGE_CASE(16)
+#undef FMHA_MERGE_CASE
+    default:
+      launch_np<0>(out_bf16, grid, stream, o_parts, lse_parts, n_parts, rows, hd, out, lse);
+  }
   return hipGetLastError();
 }
 

@@ -93,7 +93,8 @@ int fmha_mqa_fwd(const void* q, const void* k, const void* v,
  *   M = max_i lse_i,  w_i = exp(lse_i - M),
  *   out = sum_i w_i o_i / sum_i w_i,  lse = M + ln sum_i w_i.
  *  o_parts    fp32 [n_parts, rows, hd], each part normalised over its keys
- *  lse_parts  fp32 [n_parts, rows], natural log; -inf marks an empty part
+ *  lse_parts  fp32 [n_parts, rows], natural log; -inf marks an empty part,
+ *             whose o_parts values are ignored (they may hold anything)
  *  out        [rows, hd] of out_dtype; lse fp32 [rows] (may be NULL: not written)
  * A row whose parts are all empty gets out = 0, lse = -inf.
  * n_parts >= 1, rows >= 0, hd >= 4 and a multiple of 4; o_parts and out
