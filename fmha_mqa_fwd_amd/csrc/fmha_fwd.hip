@@ -1,4 +1,4 @@
-// Multi-query attention forward for gfx950 (MI355X, CDNA4).
+// Multi-query attention forward for gfx950 (MI355X, CDNA4): streaming kernel.
 //
 // What is computed follows the dev-log pages of the DeepSeek-V4 NVFP4 kernel
 // project:
@@ -11,6 +11,7 @@
 //   * keys processed tile by tile with the running O rescaled when the row
 //     maximum grows (same page, 2 "Test O Rescale at s_k > 128");
 //   * O and the row log-sum-exp as outputs (same page, "D1 Status Summary");
+//   * head dims 64/128/256 ("D1 Status Summary");
 //   * optional row gather of the s_k = top_k selected keys from a KV pool (same
 //     page "Key Numbers"; dsv4/kernels/cuda commit log, KV row gather).
 //
@@ -18,28 +19,21 @@
 //   * Head-packed M: the rows of a group (all (t, h) of a batch, or all heads of
 //     a token) share K/V, so a workgroup takes WAVES*QW consecutive rows and
 //     every K/V tile staged in LDS serves all of them.
-//   * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: K (A operand) from LDS, Q^T
-//     (B operand) in VGPRs for the whole kernel.  In the 32x32 accumulator
-//     layout lane l holds query column l%32 and 16 of the 32 keys, so a row's
-//     max/sum is an in-lane reduction plus one v_permlane32_swap, and the
-//     per-row rescale factor is a per-lane scalar.
-//   * O^T = V^T . P^T: the S^T accumulators, rounded to bf16, are the B operand
-//     of the PV MFMA as they stand (P never leaves registers).  V stays
-//     row-major in LDS; its A operand is read with ds_read_b64_tr_b16, whose
-//     16-lane transpose yields, for lane (d, half h), the keys that lane half h
-//     holds in S^T — in the same order.
-//   * Online softmax in base 2: x*scale*log2(e) folded into one FMA, exp2 on the
-//     transcendental unit, and a lazy rescale: the running maximum used for the
-//     exponentials only moves when a row's maximum grows by more than 2^8, so
-//     O and l are rescaled on a few tiles instead of every tile (exact: O and l
-//     always share the maximum they were computed against).
-//   * K/V tiles are double-buffered in LDS; the next tile's global loads are
-//     issued into registers before the current tile's MFMAs and written to the
-//     other buffer after them, so one barrier per tile suffices and load
-//     latency hides behind compute.  Two workgroups share a CU where registers
-//     allow, so one wave's softmax overlaps another's MFMAs.
-//   * LDS rows use XOR swizzles of 16-byte chunks chosen so that the MFMA operand
-//     reads and the staging writes are free of bank conflicts.
+//   * S^T = K . Q^T and O^T = V^T . P^T with v_mfma_f32_32x32x16_bf16, P kept in
+//     registers, the online softmax in-lane (fmha_device.h).
+//   * K/V tiles are moved global -> LDS by LDS-DMA buffer loads
+//     (buffer_load_dwordx4 ... lds): no staging registers, no VALU, and keys
+//     past the end of the split (or out-of-range pool rows) read as zeros from
+//     beyond the buffer descriptor.  A DMA instruction fills 1 KiB of LDS
+//     contiguously; rows are padded (K by 16 bytes for the ds_read_b128 operand
+//     reads, V by 64 bytes for the ds_read_b64_tr_b16 reads, both free of bank
+//     conflicts) and the lanes that land on pad bytes read out-of-range zeros,
+//     so every operand read is a per-lane base plus an immediate offset.
+//   * Double buffering: tile t+1 is DMA'd while tile t is computed; each buffer
+//     is its own LDS object and the loop is unrolled by two, so the compiler's
+//     DMA-completion waits stay per buffer.  One barrier per tile.
+//   * Several workgroups share a CU where registers allow, so one wave's
+//     softmax overlaps other waves' MFMAs.
 #include <type_traits>
 
 #include "fmha_device.h"
@@ -49,20 +43,19 @@ namespace {
 
 using namespace dev;
 
-// LDS row strides (bytes).  K rows are read as ds_read_b128 by 16 lanes at 16
-// consecutive rows and one column: a 16-byte pad puts those rows on 16
-// distinct bank groups.  V rows are read by ds_read_b64_tr_b16, where the 32
-// lanes of a wave half read 4 consecutive rows x 64 bytes: a 64-byte pad puts
-// the 4 rows on disjoint bank ranges.  Padding (not an XOR swizzle) keeps every
-// operand address a per-lane base plus a compile-time offset.
+// Padded LDS row strides (bytes): K rows are read as ds_read_b128 by 16 lanes
+// at 16 consecutive rows and one column (16-byte pad: 16 distinct bank
+// groups); V rows by ds_read_b64_tr_b16, whose 32-lane halves read 4
+// consecutive rows x 64 bytes (64-byte pad: 4 disjoint bank ranges).
 template <int HD>
 struct Lds {
-  static constexpr int K_STRIDE = HD * 2 + 16;
-  static constexpr int V_STRIDE = HD * 2 + 64;
+  static constexpr int ROW = HD * 2;
+  static constexpr int K_STRIDE = ROW + 16;
+  static constexpr int V_STRIDE = ROW + 64;
 };
 
-// Streaming kernel: a workgroup takes WAVES*QW rows of one group and walks the
-// keys of its split in KT-key tiles, double-buffered in LDS.
+constexpr uint32_t OOB = 0x80000000u;  // beyond any descriptor's byte count
+
 template <int HD, int QW, int KT, int WAVES, bool GATHER, int WPE>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(FwdParams p) {
@@ -70,21 +63,21 @@ void fwd_kernel(FwdParams p) {
   constexpr int NQB = QW / 32;
   constexpr int NKB = KT / 32;   // 32-key row blocks of S^T per tile
   constexpr int NKS = KT / 16;   // 16-key contraction steps of PV per tile
-  constexpr int CPR = HD / 8;    // 16-byte chunks per K/V row
   constexpr int M_WG = WAVES * QW;
-  constexpr int TILE_CH = KT * CPR;            // chunks per K (or V) tile
-  constexpr int CPT = TILE_CH / THREADS;       // chunks per thread per tile
-  constexpr int ROWS_PER_PASS = THREADS / CPR;
+  constexpr int ROW = Lds<HD>::ROW;
   constexpr int KS = Lds<HD>::K_STRIDE;
   constexpr int VS = Lds<HD>::V_STRIDE;
-  constexpr int K_BYTES = KT * KS;
-  constexpr int V_BYTES = KT * VS;
+  constexpr int NKI = (KT * KS + 1023) / 1024;   // DMA instructions per K tile
+  constexpr int NVI = (KT * VS + 1023) / 1024;   // ... per V tile
+  constexpr int KJ = (NKI + WAVES - 1) / WAVES;  // per wave (upper bound)
+  constexpr int VJ = (NVI + WAVES - 1) / WAVES;
   static_assert(QW % 32 == 0 && KT % 32 == 0 && HD % 32 == 0, "tile shape");
-  static_assert(TILE_CH % THREADS == 0 && THREADS % CPR == 0, "staging shape");
+  static_assert(KT <= THREADS, "one index per thread");
 
-  // [buf][K tile | V tile], padded rows
-  __shared__ __attribute__((aligned(16))) char smem[2][K_BYTES + V_BYTES];
-  __shared__ int sValid[GATHER ? 2 : 1][KT];
+  __shared__ __attribute__((aligned(1024))) char sK0[NKI * 1024], sK1[NKI * 1024];
+  __shared__ __attribute__((aligned(1024))) char sV0[NVI * 1024], sV1[NVI * 1024];
+  __shared__ int sIdx[GATHER ? 3 : 1][KT];    // gather: pool rows of a tile (-1 = masked)
+  __shared__ int sValid[GATHER ? 2 : 1][KT];  // gather: key usable, per K buffer
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,83 +100,94 @@ void fwd_kernel(FwdParams p) {
   const uint16_t* vbase = GATHER ? p.v : p.v + (int64_t)group * p.s_k * HD;
   const int32_t* ibase = GATHER ? p.kv_idx + (int64_t)group * p.s_k : nullptr;
 
-  // Staging assignment: chunk `sc` of tile rows srow0 + ROWS_PER_PASS*i.
-  const int sc = tid % CPR;
-  const int srow0 = tid / CPR;
+  // ---- per-lane DMA geometry (same for every tile): instruction j of this
+  // wave fills LDS bytes [1024*(wave + WAVES*j), +1024) of a tile buffer; lane
+  // `lane` of it lands in row r = pos/STRIDE at column byte c = pos%STRIDE.
+  // kr/vr: that row (-1: pad bytes or past the tile); kc/vc: the column.
+  int kr[KJ], kc[KJ], vr[VJ], vc[VJ];
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) {
+    const int inst = wave + WAVES * j;
+    const int pos = inst * 1024 + lane * 16;
+    const int r = pos / KS, cc = pos % KS;
+    const bool ok = inst < NKI && cc < ROW && r < KT;
+    kr[j] = ok ? r : -1;
+    kc[j] = cc;
+  }
+#pragma unroll
+  for (int j = 0; j < VJ; ++j) {
+    const int inst = wave + WAVES * j;
+    const int pos = inst * 1024 + lane * 16;
+    const int r = pos / VS, cc = pos % VS;
+    const bool ok = inst < NVI && cc < ROW && r < KT;
+    vr[j] = ok ? r : -1;
+    vc[j] = cc;
+  }
 
-  // ---- staging: global -> registers -> LDS, through buffer loads.  A buffer
-  // load whose offset lies beyond the descriptor's byte count returns zeros,
-  // which is how keys past the end of this split (dense) or with an
-  // out-of-range pool row (gather) become zero rows without predication.
-  u32x4 rk[CPT], rv[CPT];
-  int ridx[CPT];   // gather: pool rows of the tile being loaded (-1 = masked)
-  int rvalid[CPT];
-  constexpr uint32_t ROW_BYTES = HD * 2;
-  constexpr uint32_t OOB = 0x80000000u;  // beyond any descriptor's byte count
-  // Gather: pool-row indices of tile t (read one tile ahead of its K/V).
-  auto load_idx = [&](int t) {
-    const int t0 = key_lo + t * KT;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int key = t0 + srow0 + ROWS_PER_PASS * i;
-      ridx[i] = key < key_hi ? ibase[key] : -1;
-    }
+  // Gather: thread j < KT fetches the pool row of key j of tile t.
+  auto fetch_idx = [&](int t) __attribute__((always_inline)) {
+    const int key = key_lo + t * KT + tid;
+    int idx = -1;
+    if (tid < KT && t < n_tiles && key < key_hi) idx = ibase[key];
+    return (idx >= 0 && idx < p.pool_rows) ? idx : -1;
   };
-  auto load_tile = [&](int t) {
+
+  // DMA of tile t into (kbuf, vbuf); gather rows come from sIdx[ib].
+  auto issue = [&](int t, char* kbuf, char* vbuf, int ib) __attribute__((always_inline)) {
     const int t0 = key_lo + t * KT;
+    __amdgpu_buffer_rsrc_t rk, rv;
     if constexpr (GATHER) {
-      const auto rsk = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)p.k, (short)0, (int)((uint32_t)p.pool_rows * ROW_BYTES), BUF_FLAGS);
-      const auto rsv = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)p.v, (short)0, (int)((uint32_t)p.pool_rows * ROW_BYTES), BUF_FLAGS);
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int idx = ridx[i];
-        const bool ok = idx >= 0 && idx < p.pool_rows;
-        rvalid[i] = ok;
-        const uint32_t off = ok ? (uint32_t)idx * ROW_BYTES + 16 * sc : OOB;
-        rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsk, off, 0, 0));
-        rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsv, off, 0, 0));
-      }
+      rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, p.pool_rows * ROW, BUF_FLAGS);
+      rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, p.pool_rows * ROW, BUF_FLAGS);
     } else {
-      // descriptor covers keys t0 .. key_hi-1 of this group
-      const int nbytes = (key_hi - t0) * (int)ROW_BYTES;
-      const auto rsk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)t0 * HD),
-                                                         (short)0, nbytes, BUF_FLAGS);
-      const auto rsv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)t0 * HD),
-                                                         (short)0, nbytes, BUF_FLAGS);
+      // the descriptor covers keys t0 .. key_hi-1: later rows read as zeros
+      const int nbytes = (key_hi - t0) * ROW;
+      rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)t0 * HD), (short)0, nbytes,
+                                             BUF_FLAGS);
+      rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)t0 * HD), (short)0, nbytes,
+                                             BUF_FLAGS);
+    }
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const uint32_t off = (uint32_t)(srow0 + ROWS_PER_PASS * i) * ROW_BYTES + 16 * sc;
-        rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsk, off, 0, 0));
-        rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsv, off, 0, 0));
-        rvalid[i] = 1;
+    for (int j = 0; j < KJ; ++j) {
+      const int inst = wave + WAVES * j;
+      if (inst < NKI) {
+        uint32_t off = OOB;
+        if (kr[j] >= 0) {
+          if constexpr (GATHER) {
+            const int idx = sIdx[ib][kr[j]];
+            off = idx >= 0 ? (uint32_t)idx * ROW + kc[j] : OOB;
+          } else {
+            off = (uint32_t)kr[j] * ROW + kc[j];
+          }
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void*)(kbuf + inst * 1024), 16, off, 0, 0, 0);
       }
     }
-  };
-  // Returns nonzero when this thread staged a masked key (gather only).
-  auto store_tile = [&](int buf) {
-    int masked = 0;
-    char* sk = smem[buf];
-    char* sv = smem[buf] + K_BYTES;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int row = srow0 + ROWS_PER_PASS * i;
-      *reinterpret_cast<u32x4*>(sk + row * KS + 16 * sc) = rk[i];
-      *reinterpret_cast<u32x4*>(sv + row * VS + 16 * sc) = rv[i];
-      if constexpr (GATHER) {
-        if (sc == 0) sValid[buf][row] = rvalid[i];
-        masked |= !rvalid[i];
+    for (int j = 0; j < VJ; ++j) {
+      const int inst = wave + WAVES * j;
+      if (inst < NVI) {
+        uint32_t off = OOB;
+        if (vr[j] >= 0) {
+          if constexpr (GATHER) {
+            const int idx = sIdx[ib][vr[j]];
+            off = idx >= 0 ? (uint32_t)idx * ROW + vc[j] : OOB;
+          } else {
+            off = (uint32_t)vr[j] * ROW + vc[j];
+          }
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(vbuf + inst * 1024), 16, off, 0, 0, 0);
       }
     }
-    return masked;
   };
 
   Rows<HD, QW> w;
   w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf);
   const float c = p.scale_log2;
 
-  // Per-lane LDS byte offsets of the MFMA operands within a stage buffer.
+  // Per-lane LDS byte offsets of the MFMA operands within a tile buffer.
   //  K (A of S^T, ds_read_b128): row 32*kb + l32, bytes 32*ds + 16*hlf.
   //  V (A of O^T, ds_read_b64_tr_b16): lane (jj, dsub, hlf) of K-step ks,
   //  d block db and half r reads row 16*ks + 8*r + 4*hlf + jj/4, columns
@@ -193,62 +197,84 @@ void fwd_kernel(FwdParams p) {
   const int jj = lane & 15;
   const int dsub = (lane >> 4) & 1;
   const int k_lane = l32 * KS + 16 * hlf;
-  const int v_lane = K_BYTES + (4 * hlf + (jj >> 2)) * VS + 2 * (16 * dsub + 4 * (jj & 3));
+  const int v_lane = (4 * hlf + (jj >> 2)) * VS + 2 * (16 * dsub + 4 * (jj & 3));
 
-  int tile_masked = 0;
-  if (n_tiles > 0) {
-    if constexpr (GATHER) load_idx(0);
-    load_tile(0);
-    if constexpr (GATHER) {
-      if (n_tiles > 1) load_idx(1);
-    }
-    const int mk = store_tile(0);
-    tile_masked = GATHER ? __syncthreads_or(mk) : (__syncthreads(), 0);
-  }
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  // One tile: compute tile t from (kcur, vcur) while tile t+1 streams into
+  // (knext, vnext).  Buffers are distinct LDS objects in each unrolled copy.
+  auto step = [&](int t, const char* kcur, const char* vcur, char* knext, char* vnext, int vb)
+      __attribute__((always_inline)) {
     const int t0 = key_lo + t * KT;
     const bool have_next = t + 1 < n_tiles;
+    int idx_ahead = -1;
     if (have_next) {
-      load_tile(t + 1);
       if constexpr (GATHER) {
-        if (t + 2 < n_tiles) load_idx(t + 2);
+        // validity of tile t+1 for its K buffer, then its DMA
+        if (tid < KT) sValid[vb ^ 1][tid] = sIdx[(t + 1) % 3][tid] >= 0;
+        issue(t + 1, knext, vnext, (t + 1) % 3);
+        idx_ahead = fetch_idx(t + 2);  // written to LDS after the compute
+      } else {
+        issue(t + 1, knext, vnext, 0);
       }
     }
-    const char* sb = smem[buf];
 
     f32x16 s[NKB][NQB];
     w.template qk<NKB>(s, [&](int kb, int ds) {
-      return *reinterpret_cast<const bf16x8*>(sb + k_lane + kb * 32 * KS + ds * 32);
+      return *reinterpret_cast<const bf16x8*>(kcur + k_lane + kb * 32 * KS + ds * 32);
     });
-    if ((!GATHER && t0 + KT > key_hi) || (GATHER && tile_masked)) {
-      w.template mask<NKB>(s, hlf, [&](int kr) {
-        return GATHER ? (sValid[buf][kr] != 0) : (t0 + kr < key_hi);
+    bool masked = !GATHER && (t0 + KT > key_hi);
+    if constexpr (GATHER) masked = __any(lane < KT && !sValid[vb][lane & (KT - 1)]);
+    if (masked) {
+      w.template mask<NKB>(s, hlf, [&](int kk) {
+        return GATHER ? (sValid[vb][kk] != 0) : (t0 + kk < key_hi);
       });
     }
     bf16x8 pf[NQB][NKS];
     if (w.template softmax<NKB>(s, pf, c)) w.rescale_o();
     w.template pv<NKS>(pf, [&](int ks, int db) {
-      const char* a = sb + v_lane + 16 * ks * VS + 64 * db;
+      const char* a = vcur + v_lane + 16 * ks * VS + 64 * db;
       return v_frag_tr(a, a + 8 * VS);
     });
 
-    if (have_next) {
-      // The other buffer was last read in iteration t-1; every wave has passed
-      // the barrier that ended it.
-      const int mk = store_tile(buf ^ 1);
-      tile_masked = GATHER ? __syncthreads_or(mk) : (__syncthreads(), 0);
+    if constexpr (GATHER) {
+      if (have_next && tid < KT) sIdx[(t + 2) % 3][tid] = idx_ahead;
     }
-  }
-  // Epilogue through LDS when this workgroup's output rows fit in the stage
-  // buffers (bf16 at hd <= 128), else each lane stores its own pieces.
-  constexpr int SMEM_BYTES = 2 * (K_BYTES + V_BYTES);
-  constexpr int RB_BF16 = HD * 2;
-  if constexpr (WAVES * QW * RB_BF16 <= SMEM_BYTES) {
-    if (p.out_mode == OUT_BF16) {
+    // tile t+1 has landed (this barrier's release fence waits for every DMA)
+    // and no wave reads (kcur, vcur) any more
+    __syncthreads();
+  };
+
+  if (n_tiles > 0) {
+    if constexpr (GATHER) {
+      const int i0 = fetch_idx(0);
+      const int i1 = fetch_idx(1);
+      if (tid < KT) {
+        sIdx[0][tid] = i0;
+        sIdx[1][tid] = i1;
+        sValid[0][tid] = i0 >= 0;
+      }
       __syncthreads();
-      char* const region = &smem[0][0] + wave * QW * RB_BF16;
+    }
+    issue(0, sK0, sV0, 0);
+    if constexpr (GATHER) {
+      const int i2 = fetch_idx(2);
+      if (tid < KT) sIdx[2][tid] = i2;
+    }
+    __syncthreads();
+  }
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, sK0, sV0, sK1, sV1, 0);
+    if (t + 1 < n_tiles) step(t + 1, sK1, sV1, sK0, sV0, 1);
+  }
+
+  // Epilogue through LDS when this workgroup's output rows fit in the K tile
+  // buffers (bf16 outputs), else each lane stores its own pieces.  The last
+  // barrier of the loop has retired every read of those buffers.
+  constexpr int RB_BF16 = HD * 2;
+  constexpr int STAGE_BYTES = NKI * 1024;
+  static_assert(QW == 32, "epilogue staging assumes 32 rows per wave");
+  if constexpr (WAVES == 4 && 2 * QW * RB_BF16 <= STAGE_BYTES) {
+    if (p.out_mode == OUT_BF16) {
+      char* const region = (wave < 2 ? sK0 : sK1) + (wave & 1) * QW * RB_BF16;
       w.store_lds(p, grow0, row0, split, lane, [&](int r) { return region + r * RB_BF16; });
       return;
     }
@@ -265,7 +291,7 @@ struct Shape {
 // one wave's softmax overlaps other waves' MFMAs.  hd 256 needs the whole
 // register file: one wave per SIMD.
 Shape pick_shape(int hd, bool gather) {
-  if (hd == 256) return {32, 32, 4, 1};
+  if (hd >= 256) return {32, 32, 4, 1};
   if (gather) return {32, 64, 4, 2};
   return {32, 32, 4, 3};
 }
