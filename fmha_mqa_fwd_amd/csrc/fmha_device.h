@@ -33,11 +33,11 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr float LN2 = 0.6931471805599453f;
-// The running max used for the exponentials moves only when a row's tile max
-// exceeds it by more than this (log2 units): exponentials then stay <= 2^8,
-// far inside fp32/bf16 range, and O/l need rescaling on few tiles.  Exact: O
-// and l always share the maximum they were computed against.
-constexpr float RESCALE_THRESHOLD = 8.0f;
+// The running max used for the exponentials is left where it is while a
+// lane's sum of one tile's exponentials stays at or below this bound: every
+// exponential is then <= 2^12, far inside fp32/bf16 range, and O/l need
+// rescaling on few tiles.
+constexpr float SUM_LIMIT = 4096.0f;
 // gfx9 raw buffer descriptor word 3 (32-bit data, no swizzle, offset mode)
 constexpr int BUF_FLAGS = 0x00020000;
 
@@ -148,42 +148,67 @@ struct Rows {
       }
   }
 
-  // Online softmax of one tile in base 2 (x*scale*log2e - m in one FMA), with
-  // the lazy running max.  Writes the bf16 P^T fragments; returns whether some
-  // row's max moved (then O must be scaled by alpha before the next PV).
+  // exp2(s*c - m) of one query block's tile into the bf16 P^T fragments;
+  // returns this lane's fp32 sum of the values (before bf16 rounding, so the
+  // log-sum-exp keeps fp32 accuracy).
+  template <int NKB>
+  __device__ __forceinline__ float exps(const f32x16 (&s)[NKB][NQB], bf16x8 (&pf)[NQB][2 * NKB],
+                                        int qb, float c, float m_use) const {
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][8 * h + 2 * j], c, -m_use));
+          const float b = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][8 * h + 2 * j + 1], c, -m_use));
+          w[j] = pack_bf16x2(a, b);
+          ls0 += a;
+          ls1 += b;
+        }
+        pf[qb][2 * kb + h] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+    return ls0 + ls1;
+  }
+
+  // Online softmax of one tile in base 2 (x*scale*log2e - m in one FMA).
+  // Fast path: the exponentials are taken against the running max as it is;
+  // while no key of the tile exceeds it by much they stay small and nothing
+  // else is needed.  When a lane's sum exceeds SUM_LIMIT (or there is no max
+  // yet) the tile max is taken, the max moves, and the exponentials are redone
+  // (exact either way: O and l always share the maximum they were computed
+  // against).  Returns whether O must be scaled by alpha before the next PV.
   template <int NKB>
   __device__ __forceinline__ int softmax(f32x16 (&s)[NKB][NQB], bf16x8 (&pf)[NQB][2 * NKB],
                                          float c) {
     int any = 0;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      float mx = neg_inf();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      const float m_tile = pair_max(mx) * c;
-      const bool resc = __any(m_tile > m[qb] + RESCALE_THRESHOLD);
-      any |= resc;
-      const float m_new = resc ? fmaxf(m[qb], m_tile) : m[qb];
-      const float a = (m[qb] == neg_inf()) ? 0.f
-                      : (m_new == m[qb])   ? 1.f
-                                           : __builtin_amdgcn_exp2f(m[qb] - m_new);
-      alpha[qb] = a;
-      l[qb] *= a;
-      m[qb] = m_new;
-      const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+      bool slow = __any(m[qb] == neg_inf());
       float ls = 0.f;
+      if (!slow) {
+        ls = exps<NKB>(s, pf, qb, c, m[qb]);
+        slow = __any(!(ls <= SUM_LIMIT));
+      }
+      alpha[qb] = 1.f;
+      if (slow) {
+        float mx = neg_inf();
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        float pv[16];
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pv[r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c, -m_use));
-          ls += pv[r];
-        }
-        pf[qb][2 * kb] = pack_bf16x8(pv);
-        pf[qb][2 * kb + 1] = pack_bf16x8(pv + 8);
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+        const float m_new = fmaxf(m[qb], pair_max(mx) * c);
+        const float a = (m[qb] == neg_inf()) ? 0.f
+                        : (m_new == m[qb])   ? 1.f
+                                             : __builtin_amdgcn_exp2f(m[qb] - m_new);
+        alpha[qb] = a;
+        l[qb] *= a;
+        m[qb] = m_new;
+        any = 1;
+        ls = exps<NKB>(s, pf, qb, c, (m_new == neg_inf()) ? 0.f : m_new);
       }
       l[qb] += ls;
     }
