@@ -174,45 +174,64 @@ struct Rows {
     return ls0 + ls1;
   }
 
-  // Online softmax of one tile in base 2 (x*scale*log2e - m in one FMA).
-  // Fast path: the exponentials are taken against the running max as it is;
-  // while no key of the tile exceeds it by much they stay small and nothing
-  // else is needed.  When a lane's sum exceeds SUM_LIMIT (or there is no max
-  // yet) the tile max is taken, the max moves, and the exponentials are redone
-  // (exact either way: O and l always share the maximum they were computed
-  // against).  Returns whether O must be scaled by alpha before the next PV.
+  // Online softmax of one tile in base 2 (x*scale*log2e - m in one FMA), in
+  // two halves.  softmax_fast takes the exponentials against the running max
+  // as it is and returns (wave-uniform) whether they must be redone: some
+  // lane's sum exceeds SUM_LIMIT, or is inf/NaN because there is no max yet.
+  // softmax_slow then takes the exact tile max, moves the max, scales l and
+  // sets alpha (O must be scaled by it), and redoes the exponentials.  Exact
+  // either way: O and l always share the maximum they were computed against.
+  // commit_l adds the tile's sums to l.
+  template <int NKB>
+  __device__ __forceinline__ bool softmax_fast(const f32x16 (&s)[NKB][NQB],
+                                               bf16x8 (&pf)[NQB][2 * NKB], float c,
+                                               float (&ls)[NQB]) const {
+    bool bad = false;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      ls[qb] = exps<NKB>(s, pf, qb, c, m[qb]);
+      bad |= !(ls[qb] <= SUM_LIMIT);
+    }
+    return __any(bad);
+  }
+
+  template <int NKB>
+  __device__ __forceinline__ void softmax_slow(const f32x16 (&s)[NKB][NQB],
+                                               bf16x8 (&pf)[NQB][2 * NKB], float c,
+                                               float (&ls)[NQB]) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      float mx = neg_inf();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+      const float m_new = fmaxf(m[qb], pair_max(mx) * c);
+      const float a = (m[qb] == neg_inf()) ? 0.f
+                      : (m_new == m[qb])   ? 1.f
+                                           : __builtin_amdgcn_exp2f(m[qb] - m_new);
+      alpha[qb] = a;
+      l[qb] *= a;
+      m[qb] = m_new;
+      ls[qb] = exps<NKB>(s, pf, qb, c, (m_new == neg_inf()) ? 0.f : m_new);
+    }
+  }
+
+  __device__ __forceinline__ void commit_l(const float (&ls)[NQB]) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) l[qb] += ls[qb];
+  }
+
+  // Both halves in sequence; returns whether O must be scaled by alpha before
+  // the next PV.
   template <int NKB>
   __device__ __forceinline__ int softmax(f32x16 (&s)[NKB][NQB], bf16x8 (&pf)[NQB][2 * NKB],
                                          float c) {
-    int any = 0;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      bool slow = __any(m[qb] == neg_inf());
-      float ls = 0.f;
-      if (!slow) {
-        ls = exps<NKB>(s, pf, qb, c, m[qb]);
-        slow = __any(!(ls <= SUM_LIMIT));
-      }
-      alpha[qb] = 1.f;
-      if (slow) {
-        float mx = neg_inf();
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-        const float m_new = fmaxf(m[qb], pair_max(mx) * c);
-        const float a = (m[qb] == neg_inf()) ? 0.f
-                        : (m_new == m[qb])   ? 1.f
-                                             : __builtin_amdgcn_exp2f(m[qb] - m_new);
-        alpha[qb] = a;
-        l[qb] *= a;
-        m[qb] = m_new;
-        any = 1;
-        ls = exps<NKB>(s, pf, qb, c, (m_new == neg_inf()) ? 0.f : m_new);
-      }
-      l[qb] += ls;
-    }
-    return any;
+    float ls[NQB];
+    const bool slow = softmax_fast<NKB>(s, pf, c, ls);
+    if (slow) softmax_slow<NKB>(s, pf, c, ls);
+    commit_l(ls);
+    return slow;
   }
 
   __device__ __forceinline__ void rescale_o() {
