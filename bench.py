@@ -39,13 +39,14 @@ FLUSH_BYTES = 512 << 20
 
 # Sources the committed HBM traffic counters were taken on; a changed kernel
 # source makes those counters stale and the traffic field null.
-KERNEL_SOURCES = ["fmha_mqa_fwd_amd/csrc/fmha_fwd.hip", "fmha_mqa_fwd_amd/csrc/lse_merge.hip"]
+KERNEL_SOURCES = ["fmha_mqa_fwd_amd/csrc/fmha_fwd.hip", "fmha_mqa_fwd_amd/csrc/fmha_chunk.hip",
+                  "fmha_mqa_fwd_amd/csrc/lse_merge.hip", "fmha_mqa_fwd_amd/csrc/fmha_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # which attention kernels (by demangled name) serve each workload
 WORKLOAD_KERNEL_SIG = {
-    "mqa_prefill": lambda k: "fwd_kernel<128" in k and "false>" in k,
-    "mqa_decode": lambda k: "fwd_kernel<256" in k or "merge_kernel" in k,
-    "sparse_topk": lambda k: "fwd_kernel<128" in k and "true>" in k,
+    "mqa_prefill": lambda k: "fwd_kernel<128" in k and ", false," in k,
+    "mqa_decode": lambda k: "chunk_kernel" in k or "merge_kernel" in k,
+    "sparse_topk": lambda k: "fwd_kernel<128" in k and ", true," in k,
 }
 
 
@@ -71,6 +72,26 @@ def committed_traffic(workload: str):
     return None if ent is None else ent.get("bytes_per_launch")
 
 
+def committed_kernel_stats(workload: str):
+    """Effective clock / matrix-unit busy share of `workload`'s attention
+    kernel from the committed counter file ({} when absent or stale)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return {}
+    sig = WORKLOAD_KERNEL_SIG[workload]
+    out = {}
+    for k, v in rec.get("kernels", {}).items():
+        if sig(k) and "merge_kernel" not in k:
+            for key in ("effective_clock_GHz", "mfma_busy_frac"):
+                if key in v:
+                    out[key] = v[key]
+    return out
+
+
 CASES = (("mqa_prefill", 4), ("mqa_decode", 3), ("sparse_topk", 5))
 COPY_BYTES = 256 << 20   # calibration copy: reads and writes this many bytes
 
@@ -90,11 +111,13 @@ class Case:
         self.lse = torch.empty((w.B, w.T, w.n_h), dtype=torch.float32, device=dev)
         nb = F.workspace_bytes(w.B, w.T, w.n_h, w.hd, w.num_splits)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        # arguments marshalled once: a timed call is the C launch itself
+        self.plan = F.FwdPlan(self.q, self.k, self.v, self.idx, scale=w.scale,
+                              out_dtype=self.out_dtype, num_splits=w.num_splits,
+                              out=self.out, lse=self.lse, workspace=self.ws)
 
     def __call__(self):
-        self.F.fwd(self.q, self.k, self.v, self.idx, scale=self.w.scale,
-                   out_dtype=self.out_dtype, num_splits=self.w.num_splits,
-                   out=self.out, lse=self.lse, workspace=self.ws)
+        self.plan()
 
 
 def time_case(case, steps, warmup, flush_buf):
@@ -162,22 +185,58 @@ def _counter_rows(d):
     for fn in files:
         with open(fn) as f:
             for r in csv.DictReader(f):
+                dur = None
+                if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                    dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
                 out.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]),
-                            r.get("Dispatch_Id")))
+                            r.get("Dispatch_Id"), dur))
     return out
 
 
-def ingest_counters(fetch_dir, write_dir):
+N_XCD = 8          # GRBM_GUI_ACTIVE reads summed over the XCDs
+N_SIMD = 1024      # 256 CUs x 4 SIMDs
+
+
+def _busy_counters(d):
+    """Per fmha kernel (median dispatch): effective shader clock
+    (GRBM_GUI_ACTIVE / XCDs / dispatch duration) and the share of SIMD cycles
+    the matrix units were busy (SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x
+    GRBM_GUI_ACTIVE / XCDs))."""
+    by = {}
+    for kname, cn, val, disp, dur in _counter_rows(d):
+        if "fmha" in kname:
+            by.setdefault(kname, {}).setdefault(disp, {})[cn] = val
+            by[kname][disp]["_dur"] = dur
+    res = {}
+    for k, disps in by.items():
+        clk, mfma = [], []
+        for c in disps.values():
+            g = c.get("GRBM_GUI_ACTIVE")
+            # the dispatch timestamps are too coarse for short kernels
+            if g and c.get("_dur") and c["_dur"] > 50e-6:
+                clk.append(g / N_XCD / c["_dur"] / 1e9)
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                    mfma.append(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * g / N_XCD))
+        if clk:
+            res[k] = {"effective_clock_GHz": round(sorted(clk)[len(clk) // 2], 3)}
+            if mfma:
+                res[k]["mfma_busy_frac"] = round(sorted(mfma)[len(mfma) // 2], 4)
+    return res
+
+
+def ingest_counters(fetch_dir, write_dir, busy_dir=None):
     """Per-launch HBM bytes of each attention kernel from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
-    for a plain copy of COPY_BYTES (expected COPY_BYTES/1024 KiB each way)."""
+    for a plain copy of COPY_BYTES (expected COPY_BYTES/1024 KiB each way);
+    with busy_dir (a GRBM_GUI_ACTIVE + SQ_VALU_MFMA_BUSY_CYCLES run), also the
+    effective clock and matrix-unit busy share of each kernel."""
     rec = {"kernel_source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES,
            "workloads": {}, "kernels": {}}
     scale = {}
     per_kernel = {}
     for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         sums = {}
-        for kname, cn, val, disp in _counter_rows(d):
+        for kname, cn, val, disp, _ in _counter_rows(d):
             if cn != cname:
                 continue
             sums.setdefault(kname, []).append(val)
@@ -196,11 +255,14 @@ def ingest_counters(fetch_dir, write_dir):
             "fetch_kib_raw": kib_f, "write_kib_raw": kib_w,
             "bytes_per_launch": kib_f * 1024 * scale["FETCH_SIZE"] + kib_w * 1024 * scale["WRITE_SIZE"]}
     rec["copy_scale"] = scale
+    if busy_dir:
+        for k, b in _busy_counters(busy_dir).items():
+            rec["kernels"].setdefault(k, {}).update(b)
     # map kernels to workloads: the attention kernel with the largest traffic
     # of each workload's run is recorded by its template signature
     for name, _ in CASES:
         sig = WORKLOAD_KERNEL_SIG.get(name)
-        tot = sum(v["bytes_per_launch"] for k, v in rec["kernels"].items() if sig and sig(k))
+        tot = sum(v.get("bytes_per_launch", 0) for k, v in rec["kernels"].items() if sig and sig(k))
         if tot:
             rec["workloads"][name] = {"bytes_per_launch": tot}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
@@ -208,6 +270,59 @@ def ingest_counters(fetch_dir, write_dir):
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec, indent=1))
+
+
+def copy_ceiling(dev, nbytes=1 << 30, reps=10):
+    """Practical HBM ceiling: a plain device-to-device copy of `nbytes`
+    (read + write bytes per second, median of `reps`)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * nbytes / sorted(ts)[len(ts) // 2] / 1e9
+
+
+def trace_summary(trace_csv):
+    """Markdown table of per-kernel durations from a rocprofv3 --kernel-trace
+    CSV of a bench.py run: all dispatches, and the timed flushed calls alone
+    (each dispatch that directly follows the cache-flush reduction)."""
+    import csv
+
+    with open(trace_csv) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    allk, flushed = {}, {}
+    prev = None
+    for r in rows:
+        name = r["Kernel_Name"]
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+        allk.setdefault(name, []).append(us)
+        if prev is not None and "reduce_kernel" in prev["Kernel_Name"] and "reduce_kernel" not in name:
+            flushed.setdefault(name, []).append(us)
+        prev = r
+
+    def short(n):
+        n = n.replace("void fmha::(anonymous namespace)::", "").split("(fmha::")[0]
+        return n.split("(float const*")[0][:70]
+
+    lines = ["| kernel | dispatches | avg us | min us | max us | flushed calls | flushed avg us |",
+             "|---|---|---|---|---|---|---|"]
+    for name, v in sorted(allk.items(), key=lambda kv: -sum(kv[1])):
+        if "fmha" not in name and "copyBuffer" not in name:
+            continue
+        fl = flushed.get(name, [])
+        fl_avg = f"{sum(fl) / len(fl):.1f}" if fl else "-"
+        lines.append(f"| `{short(name)}` | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | "
+                     f"{max(v):.1f} | {len(fl)} | {fl_avg} |")
+    return "\n".join(lines)
 
 
 def cpu_baseline(budget_s=12.0):
@@ -250,11 +365,20 @@ def main():
                     help="profile mode: run one workload back to back, no JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="profile mode: also run a plain device copy of known size")
-    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
-                         "--only ... --copy-calibration into " + TRAFFIC_FILE)
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="print per-kernel durations (all / flushed calls) of a "
+                         "rocprofv3 --kernel-trace run of bench.py")
+    ap.add_argument("--ingest-counters", nargs="+", metavar="DIR",
+                    help="FETCH_DIR WRITE_DIR [BUSY_DIR]: turn rocprofv3 --pmc runs "
+                         "(FETCH_SIZE; WRITE_SIZE; GRBM_GUI_ACTIVE + SQ_VALU_MFMA_BUSY_CYCLES) "
+                         "of --only ... --copy-calibration into " + TRAFFIC_FILE)
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
     if args.ingest_counters:
+        if len(args.ingest_counters) not in (2, 3):
+            ap.error("--ingest-counters takes FETCH_DIR WRITE_DIR [BUSY_DIR]")
         ingest_counters(*args.ingest_counters)
         return
     if args.gpus != 1:
@@ -299,6 +423,9 @@ def main():
         del case
         torch.cuda.empty_cache()
 
+    copy_gbps = copy_ceiling(dev)
+    print(f"[bench] device copy: {copy_gbps:.0f} GB/s (read + write)", file=sys.stderr, flush=True)
+
     p, d, s = res["mqa_prefill"], res["mqa_decode"], res["sparse_topk"]
     traffic = committed_traffic("mqa_prefill")
     line = {
@@ -325,6 +452,7 @@ def main():
                    "us_per_call": round(d["ms"] * 1e3, 2),
                    "us_per_call_warm": round(d["ms_warm"] * 1e3, 2),
                    "algorithmic_bytes": d["bytes"], "workload": d["workload"],
+                   "hbm_copy_GBps": round(copy_gbps, 1),
                    "traffic": committed_traffic("mqa_decode")},
         "sparse_topk": {"value": round(s["tflops"], 2), "unit": "TFLOP/s",
                         "frac_of_mfma_peak": round(s["tflops"] / PEAK_BF16_TFLOPS, 4),
@@ -336,7 +464,8 @@ def main():
                            "us_median": round(p["ms_median"] * 1e3, 2),
                            "us_p10": round(p["ms_p10"] * 1e3, 2),
                            "us_p90": round(p["ms_p90"] * 1e3, 2),
-                           "us_per_call_warm": round(p["ms_warm"] * 1e3, 2)},
+                           "us_per_call_warm": round(p["ms_warm"] * 1e3, 2),
+                           **committed_kernel_stats("mqa_prefill")},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()

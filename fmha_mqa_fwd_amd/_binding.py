@@ -87,6 +87,66 @@ def workspace_bytes(B: int, T: int, n_h: int, hd: int, num_splits: int) -> int:
     return int(_lib.fmha_mqa_workspace_bytes(B, T, n_h, hd, num_splits))
 
 
+class FwdPlan:
+    """fmha_mqa_fwd with its arguments checked and marshalled once.
+
+    Calling the plan launches the forward again on the same tensors and
+    stream (for loops and timing, where per-call Python work would otherwise
+    sit between launches); it returns (out, lse).  Arguments as for `fwd`.
+    """
+
+    def __init__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 kv_idx: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                 out_dtype: torch.dtype = torch.bfloat16, num_splits: int = 1,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+        if q.dim() != 4:
+            raise ValueError("q must be [B, T, n_h, hd]")
+        B, T, n_h, hd = q.shape
+        if kv_idx is None:
+            if k.dim() != 3 or k.shape[0] != B or k.shape[2] != hd or v.shape != k.shape:
+                raise ValueError("dense k/v must be [B, s_k, hd] with q's B and hd")
+            s_k, pool_rows = k.shape[1], 0
+        else:
+            if k.dim() != 2 or k.shape[1] != hd or v.shape != k.shape:
+                raise ValueError("gather k/v pools must be [P, hd] with q's hd")
+            if kv_idx.dtype != torch.int32 or tuple(kv_idx.shape[:2]) != (B, T) or kv_idx.dim() != 3:
+                raise ValueError("kv_idx must be int32 [B, T, s_k]")
+            s_k, pool_rows = kv_idx.shape[2], k.shape[0]
+            if not kv_idx.is_contiguous():
+                raise ValueError("kv_idx must be contiguous")
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if t.dtype != torch.bfloat16:
+                raise ValueError(f"{name} must be bfloat16")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        dev = q.device
+        if scale is None:
+            scale = default_scale(hd)
+        if out is None:
+            out = torch.empty((B, T, n_h, hd), dtype=out_dtype, device=dev)
+        if lse is None:
+            lse = torch.empty((B, T, n_h), dtype=torch.float32, device=dev)
+        ws_need = workspace_bytes(B, T, n_h, hd, num_splits)
+        if workspace is None and ws_need > 0:
+            workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        # keep every tensor the launch reads or writes alive with the plan
+        self._keep = (q, k, v, kv_idx, workspace)
+        self.out, self.lse = out, lse
+        self._fn = _lib.fmha_mqa_fwd
+        self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(out), _ptr(lse),
+                      B, T, n_h, s_k, hd, pool_rows, float(scale),
+                      _dtype_code(out.dtype), int(num_splits), _ptr(workspace), ws_bytes,
+                      _stream_handle(stream))
+
+    def __call__(self) -> Tuple[torch.Tensor, torch.Tensor]:
+        st = self._fn(*self._args)
+        if st != 0:
+            raise FmhaError("fmha_mqa_fwd", st)
+        return self.out, self.lse
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         kv_idx: Optional[torch.Tensor] = None, scale: Optional[float] = None,
         out_dtype: torch.dtype = torch.bfloat16, num_splits: int = 1,
@@ -98,44 +158,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     q [B, T, n_h, hd] bf16; dense k, v [B, s_k, hd] bf16, or pools [P, hd] with
     kv_idx [B, T, s_k] int32.  Returns (out [B, T, n_h, hd], lse [B, T, n_h] fp32).
     """
-    if q.dim() != 4:
-        raise ValueError("q must be [B, T, n_h, hd]")
-    B, T, n_h, hd = q.shape
-    if kv_idx is None:
-        if k.dim() != 3 or k.shape[0] != B or k.shape[2] != hd or v.shape != k.shape:
-            raise ValueError("dense k/v must be [B, s_k, hd] with q's B and hd")
-        s_k, pool_rows = k.shape[1], 0
-    else:
-        if k.dim() != 2 or k.shape[1] != hd or v.shape != k.shape:
-            raise ValueError("gather k/v pools must be [P, hd] with q's hd")
-        if kv_idx.dtype != torch.int32 or tuple(kv_idx.shape[:2]) != (B, T) or kv_idx.dim() != 3:
-            raise ValueError("kv_idx must be int32 [B, T, s_k]")
-        s_k, pool_rows = kv_idx.shape[2], k.shape[0]
-        if not kv_idx.is_contiguous():
-            raise ValueError("kv_idx must be contiguous")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{name} must be bfloat16")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    dev = q.device
-    if scale is None:
-        scale = default_scale(hd)
-    if out is None:
-        out = torch.empty((B, T, n_h, hd), dtype=out_dtype, device=dev)
-    if lse is None:
-        lse = torch.empty((B, T, n_h), dtype=torch.float32, device=dev)
-    ws_need = workspace_bytes(B, T, n_h, hd, num_splits)
-    if workspace is None and ws_need > 0:
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _lib.fmha_mqa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(out), _ptr(lse),
-                           B, T, n_h, s_k, hd, pool_rows, float(scale),
-                           _dtype_code(out.dtype), int(num_splits), _ptr(workspace), ws_bytes,
-                           _stream_handle(stream))
-    if st != 0:
-        raise FmhaError("fmha_mqa_fwd", st)
-    return out, lse
+    return FwdPlan(q, k, v, kv_idx, scale, out_dtype, num_splits, out, lse, workspace, stream)()
 
 
 def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,

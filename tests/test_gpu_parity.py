@@ -248,6 +248,25 @@ def test_runs_on_a_side_stream(F):
     _check(out, lse, q, k, v, None, w.scale)
 
 
+def test_plan_relaunches_on_the_same_tensors(F):
+    """FwdPlan (arguments marshalled once) matches fwd on every relaunch,
+    also after its inputs change in place."""
+    w = W.make_custom(B=2, T=4, n_h=64, hd=128, s_k=300, out_dtype="bf16", num_splits=3, seed=8)
+    q, k, v, idx = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    plan = F.FwdPlan(qd, kd, vd, scale=w.scale, out_dtype=torch.bfloat16, num_splits=3)
+    for _ in range(2):
+        out, lse = plan()
+        torch.cuda.synchronize()
+        _check(out, lse, q, k, v, None, w.scale)
+    v2 = (v.float() * -0.5).to(torch.bfloat16)
+    vd.copy_(v2)
+    out, lse = plan()
+    torch.cuda.synchronize()
+    _check(out, lse, q, k, v2, None, w.scale)
+
+
 # --------------------------------------------------------------- the merge
 @pytest.mark.parametrize("hd,out_dtype", [(64, "f32"), (128, "bf16"), (256, "f32"), (20, "f32")])
 def test_lse_merge_entry_point(F, hd, out_dtype):
