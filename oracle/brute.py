@@ -7,6 +7,10 @@ Pipeline + Production", "Key lessons from this session"), the max-shifted
 exponentials, ``math.fsum`` for every sum, ``O = sum_j p_j V_j`` and
 ``lse = m + ln sum_j exp(x_j - m)``.  It is only run on tiny shapes, where its
 exactly rounded sums make it the tie-breaker for ``oracle.fp64``.
+
+With a sink (one logit per query head, zero value vector; the reading of the
+sink merge named on page "May 24, 2026 — Session Start Plan") the sink logit is
+one more term of the softmax's denominator.
 """
 from __future__ import annotations
 
@@ -15,22 +19,22 @@ import math
 __all__ = ["brute_attention", "brute_merge"]
 
 
-def _row(qr, keys, vals, scale):
+def _row(qr, keys, vals, scale, sink=-math.inf):
     xs = [scale * math.fsum(a * b for a, b in zip(qr, kj)) for kj in keys]
     if not xs:
-        return [0.0] * len(vals[0]) if vals else [], -math.inf
-    m = max(xs)
+        return [0.0] * len(vals[0]) if vals else [], sink
+    m = max(xs + [sink])
     es = [math.exp(x - m) for x in xs]
-    l = math.fsum(es)
+    l = math.fsum(es + [math.exp(sink - m)])
     hd = len(vals[0])
     o = [math.fsum(es[j] * vals[j][d] for j in range(len(es))) / l for d in range(hd)]
     return o, m + math.log(l)
 
 
-def brute_attention(q, k, v, scale, kv_idx=None):
+def brute_attention(q, k, v, scale, kv_idx=None, sink=None):
     """q nested lists [B][T][n_h][hd]; dense k, v [B][s_k][hd]; gather k, v
-    [P][hd] with kv_idx [B][T][s_k].  Returns (O [B][T][n_h][hd], lse [B][T][n_h])
-    as nested Python lists of floats."""
+    [P][hd] with kv_idx [B][T][s_k]; optional sink [n_h].  Returns
+    (O [B][T][n_h][hd], lse [B][T][n_h]) as nested Python lists of floats."""
     O, L = [], []
     for b in range(len(q)):
         Ob, Lb = [], []
@@ -42,7 +46,8 @@ def brute_attention(q, k, v, scale, kv_idx=None):
                 vals = [v[i] for i in kv_idx[b][t]]
             Ot, Lt = [], []
             for h in range(len(q[b][t])):
-                o, lse = _row(q[b][t][h], keys, vals, scale)
+                o, lse = _row(q[b][t][h], keys, vals, scale,
+                              -math.inf if sink is None else sink[h])
                 Ot.append(o)
                 Lt.append(lse)
             Ob.append(Ot)

@@ -23,6 +23,13 @@ NVFP4 kernel project):
   (Multi-KV-tile).  It is exact only when every O_i is normalised over the keys
   of its own part, which is the reading taken here; the merged LSE is then
   ``ln sum_i exp(lse_i)``, the LSE over all keys.
+* Attention sink — page "May 24, 2026 — Session Start Plan" lists a "sink
+  merge" (File Map: the decode op holds the "Sink merge formula"; D1 Status
+  Summary: "D5b (Python sink merge)") without printing it.  Reading taken: a
+  sink is one extra logit per query head, in the units of the scaled logits,
+  whose value vector is zero.  It joins the softmax's denominator and nothing
+  else: ``lse = ln(sum_j exp(x_j) + exp(sink_h))``, ``O = sum_j exp(x_j - lse)
+  V_j``; ``sink_h = -inf`` is no sink.
 * Selected keys — a row attends to s_k = top_k keys picked from a KV store: page
   "May 24, 2026 — Session Start Plan", "Key Numbers" (top_k 1024 -> s_k 1024),
   and the ``dsv4/kernels/cuda`` commit log (KV row gather, 32768-row pool).
@@ -79,20 +86,28 @@ def attention_probs(q_rows: np.ndarray, K: np.ndarray, scale: float) -> np.ndarr
 
 
 def attention_rows(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
-                   scale: float):
+                   scale: float, sink_rows=None):
     """Attention of independent query rows against one shared K/V set.
 
     q_rows [R, hd], K [S, hd], V [S, hd]  ->  (O [R, hd], lse [R]).
     O[r] = sum_j p_rj V[j];  lse[r] = m_r + ln sum_j exp(x_rj - m_r).
     S = 0 gives O = 0 and lse = -inf (empty part).
+    sink_rows [R] (optional): each row's sink logit, one more term of the
+    softmax's denominator with a zero value vector (-inf: none).
     """
     R, hd = q_rows.shape
+    sink = None if sink_rows is None else np.asarray(sink_rows, np.float64).reshape(R, 1)
     if K.shape[0] == 0:
-        return np.zeros((R, V.shape[1]), np.float64), np.full(R, -np.inf)
+        lse = np.full(R, -np.inf) if sink is None else sink[:, 0].copy()
+        return np.zeros((R, V.shape[1]), np.float64), lse
     x = _logits(q_rows, K, scale)
     m = x.max(axis=1, keepdims=True)
+    if sink is not None:
+        m = np.maximum(m, sink)
     e = np.exp(x - m)
     l = e.sum(axis=1, keepdims=True)
+    if sink is not None:
+        l = l + np.exp(sink - m)
     o = (e / l) @ V
     lse = m[:, 0] + np.log(l[:, 0])
     return o, lse
@@ -106,7 +121,7 @@ def _kv_for_group(k, v, kv_idx, b, t):
 
 
 def attention(q, k, v, scale: float, kv_idx=None, rows=None,
-              key_range=None):
+              key_range=None, sink=None):
     """Multi-query attention forward in float64.
 
     q [B, T, n_h, hd]; dense: k, v [B, s_k, hd]; gather: k, v [P, hd] pools and
@@ -116,6 +131,8 @@ def attention(q, k, v, scale: float, kv_idx=None, rows=None,
     result is then [len(rows), hd] / [len(rows)] in the given order.
     key_range: optional (lo, hi) restricting attention to keys lo..hi-1 of each
     row's key list (used to form split partials).
+    sink: optional [n_h] sink logits (natural-log units, -inf = none), one per
+    query head.
 
     Returns (O, lse) as float64; full shape [B, T, n_h, hd] and [B, T, n_h].
     """
@@ -123,6 +140,7 @@ def attention(q, k, v, scale: float, kv_idx=None, rows=None,
     k = to_f64(k)
     v = to_f64(v)
     kv_idx = to_f64(kv_idx)
+    sink = None if sink is None else to_f64(sink).reshape(-1)
     B, T, n_h, hd = q.shape
     dv = v.shape[-1]
     if rows is None:
@@ -147,7 +165,8 @@ def attention(q, k, v, scale: float, kv_idx=None, rows=None,
             K, V = K[key_range[0]:key_range[1]], V[key_range[0]:key_range[1]]
         for c0 in range(0, grp.size, _CHUNK_ROWS):
             sel = grp[c0:c0 + _CHUNK_ROWS]
-            o, lse = attention_rows(qf[flat[sel]], K, V, scale)
+            o, lse = attention_rows(qf[flat[sel]], K, V, scale,
+                                    None if sink is None else sink[flat[sel] % n_h])
             O[sel] = o
             L[sel] = lse
     if rows is None:

@@ -308,40 +308,125 @@ def _mutants():
 
     good = A.attention_rows
 
-    def no_scale(q, K, V, s):
-        return good(q, K, V, 1.0)
+    def no_scale(q, K, V, s, sink_rows=None):
+        return good(q, K, V, 1.0, sink_rows)
 
-    def lse_log2(q, K, V, s):
-        o, l = good(q, K, V, s)
+    def lse_log2(q, K, V, s, sink_rows=None):
+        o, l = good(q, K, V, s, sink_rows)
         return o, l / math.log(2.0)
 
-    def unnormalised(q, K, V, s):
+    def unnormalised(q, K, V, s, sink_rows=None):
         x = s * (q @ K.T)
         m = x.max(axis=1, keepdims=True)
         e = np.exp(x - m)
         return e @ V, m[:, 0] + np.log(e.sum(axis=1))
 
-    def transposed_v(q, K, V, s):
-        o, l = good(q, K, V[::-1], s)
+    def transposed_v(q, K, V, s, sink_rows=None):
+        o, l = good(q, K, V[::-1], s, sink_rows)
         return o, l
 
-    def wrong_sign(q, K, V, s):
-        return good(q, -K, V, s)
+    def wrong_sign(q, K, V, s, sink_rows=None):
+        return good(q, -K, V, s, sink_rows)
 
-    def lse_without_max(q, K, V, s):
-        o, l = good(q, K, V, s)
+    def lse_without_max(q, K, V, s, sink_rows=None):
+        o, l = good(q, K, V, s, sink_rows)
         x = s * (q @ K.T)
         return o, l - x.max(axis=1)
 
+    def sink_ignored(q, K, V, s, sink_rows=None):
+        return good(q, K, V, s)
+
+    def sink_value_one(q, K, V, s, sink_rows=None):
+        # the sink's value vector taken as ones instead of zeros
+        o, l = good(q, K, V, s, sink_rows)
+        if sink_rows is None:
+            return o, l
+        return o + np.exp(np.asarray(sink_rows, np.float64) - l)[:, None], l
+
     return {"no_scale": no_scale, "lse_log2": lse_log2, "unnormalised": unnormalised,
             "reversed_v": transposed_v, "wrong_sign": wrong_sign,
-            "lse_without_max": lse_without_max}
+            "lse_without_max": lse_without_max, "sink_ignored": sink_ignored,
+            "sink_value_one": sink_value_one}
+
+
+# ------------------------------------------------------------ attention sink
+# Reading (page "May 24, 2026 — Session Start Plan", File Map and D1 Status
+# Summary name a "sink merge" without its formula): one extra logit per query
+# head with a zero value vector.
+
+
+def _sinks(n_h, seed):
+    g = np.random.default_rng(seed)
+    s = g.normal(0.0, 2.0, n_h)
+    s[0] = -np.inf  # the first head has no sink
+    return s
+
+
+@pytest.mark.parametrize("B,T,n_h,s_k,hd", [(1, 2, 3, 4, 3), (2, 1, 2, 1, 5), (1, 1, 4, 7, 2)])
+def test_sink_matches_brute_force(B, T, n_h, s_k, hd):
+    w = W.make_custom(B=B, T=T, n_h=n_h, hd=hd, s_k=s_k, out_dtype="f32", seed=50 + s_k)
+    q, k, v, _ = W.make_inputs(w)
+    sink = _sinks(n_h, s_k)
+    O, L = oracle.attention(q, k, v, 0.7, sink=sink)
+    Ob, Lb = brute.brute_attention(_tolist(oracle.to_f64(q)), _tolist(oracle.to_f64(k)),
+                                   _tolist(oracle.to_f64(v)), 0.7, sink=list(sink))
+    np.testing.assert_allclose(O, np.array(Ob), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, np.array(Lb), rtol=1e-13, atol=1e-12)
+
+
+def test_sink_is_an_extra_key_with_zero_value():
+    """For one query row, a sink logit s equals appending the key
+    k* = q * s / (scale |q|^2) (its logit is exactly s) with value 0."""
+    g = np.random.default_rng(7)
+    hd, s_k, scale = 6, 5, 0.4
+    q = g.normal(size=(1, 1, 1, hd))
+    k = g.normal(size=(1, s_k, hd))
+    v = g.normal(size=(1, s_k, hd))
+    for s in (-3.0, 0.5, 4.0, 30.0):
+        kstar = q[0, 0, 0] * s / (scale * float(q[0, 0, 0] @ q[0, 0, 0]))
+        k2 = np.concatenate([k, kstar[None, None, :]], axis=1)
+        v2 = np.concatenate([v, np.zeros((1, 1, hd))], axis=1)
+        O_ref, L_ref = oracle.attention(q, k2, v2, scale)
+        O, L = oracle.attention(q, k, v, scale, sink=np.array([s]))
+        np.testing.assert_allclose(O, O_ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L, L_ref, rtol=1e-13, atol=1e-12)
+
+
+def test_sink_minus_inf_changes_nothing():
+    w = W.make_custom(B=2, T=3, n_h=2, hd=8, s_k=9, out_dtype="f32", seed=61)
+    q, k, v, idx = W.make_inputs(w)
+    O0, L0 = oracle.attention(q, k, v, w.scale)
+    O1, L1 = oracle.attention(q, k, v, w.scale, sink=np.full(2, -np.inf))
+    assert np.array_equal(O0, O1) and np.array_equal(L0, L1)
+
+
+def test_dominant_sink_empties_the_row():
+    """A sink 60 above every logit: O within e^-60 of zero, lse = sink."""
+    w = W.make_custom(B=1, T=2, n_h=2, hd=8, s_k=9, out_dtype="f32", seed=62)
+    q, k, v, _ = W.make_inputs(w)
+    O0, L0 = oracle.attention(q, k, v, w.scale)
+    sink = np.full(2, float(L0.max()) + 60.0)
+    O, L = oracle.attention(q, k, v, w.scale, sink=sink)
+    assert np.abs(O).max() <= math.exp(-60) * np.abs(oracle.to_f64(v)).max() * 2
+    np.testing.assert_allclose(L, np.broadcast_to(sink, L.shape), rtol=1e-15, atol=1e-12)
+
+
+def test_sink_without_keys_gives_the_sink_lse():
+    q = np.ones((1, 1, 2, 4))
+    k = np.zeros((1, 0, 4))
+    O, L = oracle.attention(q, k, k.copy(), 0.5, sink=np.array([1.5, -np.inf]))
+    assert np.all(O == 0) and L[0, 0, 0] == 1.5 and L[0, 0, 1] == -np.inf
+
+
+def _sink_pin():
+    test_sink_matches_brute_force(1, 2, 3, 4, 3)
+    test_sink_is_an_extra_key_with_zero_value()
 
 
 _PIN_CHECKS = [test_two_key_worked_example, test_uniform_v_gives_v,
                test_uniform_k_gives_mean_and_log_count, test_single_key_gives_that_value_row,
                lambda: test_dense_matches_brute_force(2, 3, 2, 5, 8),
-               lambda: test_dense_matches_torch_sdpa_fp64(2, 5, 3, 37, 16)]
+               lambda: test_dense_matches_torch_sdpa_fp64(2, 5, 3, 37, 16), _sink_pin]
 
 
 @pytest.mark.parametrize("name", sorted(_mutants()))
