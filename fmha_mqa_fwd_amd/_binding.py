@@ -26,6 +26,12 @@ SIGNATURES = {
     "fmha_mqa_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                               _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                               _c_int, _c_int, _c_void_p, _c_size, _c_void_p]),
+    "fmha_mqa_fwd_sink": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   _c_float, _c_int, _c_int, _c_void_p, _c_size, _c_void_p,
+                                   _c_void_p]),
+    "fmha_attention_sink": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int,
+                                     _c_int, _c_void_p]),
     "fmha_lse_merge": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
                                 _c_int, _c_void_p, _c_void_p]),
     "fmha_status_string": (ctypes.c_char_p, [_c_int]),
@@ -99,7 +105,8 @@ class FwdPlan:
                  kv_idx: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                  out_dtype: torch.dtype = torch.bfloat16, num_splits: int = 1,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None, stream=None):
+                 workspace: Optional[torch.Tensor] = None, stream=None,
+                 sink: Optional[torch.Tensor] = None):
         if q.dim() != 4:
             raise ValueError("q must be [B, T, n_h, hd]")
         B, T, n_h, hd = q.shape
@@ -120,6 +127,9 @@ class FwdPlan:
                 raise ValueError(f"{name} must be bfloat16")
             if not t.is_contiguous():
                 raise ValueError(f"{name} must be contiguous")
+        if sink is not None:
+            if sink.dtype != torch.float32 or sink.shape != (n_h,) or not sink.is_contiguous():
+                raise ValueError("sink must be a contiguous float32 [n_h] tensor")
         dev = q.device
         if scale is None:
             scale = default_scale(hd)
@@ -132,18 +142,20 @@ class FwdPlan:
             workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         # keep every tensor the launch reads or writes alive with the plan
-        self._keep = (q, k, v, kv_idx, workspace)
+        self._keep = (q, k, v, kv_idx, workspace, sink)
         self.out, self.lse = out, lse
-        self._fn = _lib.fmha_mqa_fwd
+        self._fn = _lib.fmha_mqa_fwd if sink is None else _lib.fmha_mqa_fwd_sink
         self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(out), _ptr(lse),
                       B, T, n_h, s_k, hd, pool_rows, float(scale),
                       _dtype_code(out.dtype), int(num_splits), _ptr(workspace), ws_bytes,
                       _stream_handle(stream))
+        if sink is not None:
+            self._args = self._args + (_ptr(sink),)
 
     def __call__(self) -> Tuple[torch.Tensor, torch.Tensor]:
         st = self._fn(*self._args)
         if st != 0:
-            raise FmhaError("fmha_mqa_fwd", st)
+            raise FmhaError(self._fn.__name__, st)
         return self.out, self.lse
 
 
@@ -151,14 +163,35 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         kv_idx: Optional[torch.Tensor] = None, scale: Optional[float] = None,
         out_dtype: torch.dtype = torch.bfloat16, num_splits: int = 1,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-        workspace: Optional[torch.Tensor] = None, stream=None
-        ) -> Tuple[torch.Tensor, torch.Tensor]:
+        workspace: Optional[torch.Tensor] = None, stream=None,
+        sink: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Multi-query attention forward (see include/fmha_mqa.h).
 
     q [B, T, n_h, hd] bf16; dense k, v [B, s_k, hd] bf16, or pools [P, hd] with
     kv_idx [B, T, s_k] int32.  Returns (out [B, T, n_h, hd], lse [B, T, n_h] fp32).
+    With sink (fp32 [n_h]) the attention sink joins every row
+    (fmha_mqa_fwd_sink).
     """
-    return FwdPlan(q, k, v, kv_idx, scale, out_dtype, num_splits, out, lse, workspace, stream)()
+    return FwdPlan(q, k, v, kv_idx, scale, out_dtype, num_splits, out, lse, workspace, stream,
+                   sink)()
+
+
+def apply_sink(out: torch.Tensor, lse: torch.Tensor, sink: torch.Tensor, stream=None
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fmha_attention_sink in place: out [..., n_h, hd] (fp32 or bf16) and lse
+    [..., n_h] of finished rows; sink fp32 [n_h].  Returns (out, lse)."""
+    if out.dim() < 2 or lse.shape != out.shape[:-1]:
+        raise ValueError("out must be [..., n_h, hd] and lse [..., n_h]")
+    n_h, hd = out.shape[-2], out.shape[-1]
+    if sink.dtype != torch.float32 or sink.shape != (n_h,) or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous float32 [n_h] tensor")
+    if lse.dtype != torch.float32 or not (out.is_contiguous() and lse.is_contiguous()):
+        raise ValueError("out and lse must be contiguous; lse float32")
+    st = _lib.fmha_attention_sink(_ptr(out), _ptr(lse), _ptr(sink), lse.numel(), n_h, hd,
+                                  _dtype_code(out.dtype), _stream_handle(stream))
+    if st != 0:
+        raise FmhaError("fmha_attention_sink", st)
+    return out, lse
 
 
 def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,

@@ -36,21 +36,11 @@ inline WsLayout ws_layout(int64_t rows, int hd, int splits) {
 
 inline int launch_status(hipError_t e) { return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH; }
 
-}  // namespace
-
-extern "C" {
-
-size_t fmha_mqa_workspace_bytes(int B, int T, int n_h, int hd, int num_splits) {
-  if (B < 0 || T < 0 || n_h < 0 || hd <= 0 || num_splits < 1) return 0;
-  if (num_splits == 1) return 0;
-  const int64_t rows = (int64_t)B * T * n_h;
-  return ws_layout(rows, hd, num_splits).total;
-}
-
-int fmha_mqa_fwd(const void* q, const void* k, const void* v, const int32_t* kv_idx, void* out,
-                 float* lse, int B, int T, int n_h, int s_k, int hd, int pool_rows, float scale,
-                 int out_dtype, int num_splits, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+// The forward of fmha_mqa_fwd / fmha_mqa_fwd_sink (sink: nullptr or [n_h]).
+int fwd_impl(const void* q, const void* k, const void* v, const int32_t* kv_idx, void* out,
+             float* lse, int B, int T, int n_h, int s_k, int hd, int pool_rows, float scale,
+             int out_dtype, int num_splits, void* workspace, size_t workspace_bytes,
+             void* stream, const float* sink) {
   if (out_dtype != FMHA_F32 && out_dtype != FMHA_BF16) return FMHA_ERR_INVALID_ARG;
   if (B < 0 || T < 0 || n_h < 0 || s_k < 0 || num_splits < 1) return FMHA_ERR_INVALID_ARG;
   if (hd != 64 && hd != 128 && hd != 256) return FMHA_ERR_UNSUPPORTED;
@@ -72,6 +62,7 @@ int fmha_mqa_fwd(const void* q, const void* k, const void* v, const int32_t* kv_
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4)) return FMHA_ERR_ALIGNMENT;
   if (s_k > 0 && (!aligned(k, 16) || !aligned(v, 16))) return FMHA_ERR_ALIGNMENT;
   if (gather && !aligned(kv_idx, 4)) return FMHA_ERR_ALIGNMENT;
+  if (sink && !aligned(sink, 4)) return FMHA_ERR_ALIGNMENT;
 
   fmha::FwdParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -86,6 +77,8 @@ int fmha_mqa_fwd(const void* q, const void* k, const void* v, const int32_t* kv_
   p.num_splits = num_splits;
   p.chunk = (s_k + num_splits - 1) / num_splits;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.sink = sink;
+  p.n_heads = n_h;
   if (gather && s_k == 0) p.n_groups = B * T;  // still one group per token
 
   const int64_t grid = fmha::fwd_grid_size(p, hd);
@@ -111,8 +104,50 @@ int fmha_mqa_fwd(const void* q, const void* k, const void* v, const int32_t* kv_
   p.out_mode = fmha::OUT_PARTIAL;
   int s = launch_status(fmha::launch_fwd(p, hd, st));
   if (s != FMHA_OK) return s;
+  // the sink joins once, in the merge (the partials carry none)
   return launch_status(fmha::launch_merge(o_part, lse_part, num_splits, (int)rows, hd, out,
-                                          out_dtype == FMHA_BF16, lse, st));
+                                          out_dtype == FMHA_BF16, lse, st, sink, n_h));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fmha_mqa_workspace_bytes(int B, int T, int n_h, int hd, int num_splits) {
+  if (B < 0 || T < 0 || n_h < 0 || hd <= 0 || num_splits < 1) return 0;
+  if (num_splits == 1) return 0;
+  const int64_t rows = (int64_t)B * T * n_h;
+  return ws_layout(rows, hd, num_splits).total;
+}
+
+int fmha_mqa_fwd(const void* q, const void* k, const void* v, const int32_t* kv_idx, void* out,
+                 float* lse, int B, int T, int n_h, int s_k, int hd, int pool_rows, float scale,
+                 int out_dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return fwd_impl(q, k, v, kv_idx, out, lse, B, T, n_h, s_k, hd, pool_rows, scale, out_dtype,
+                  num_splits, workspace, workspace_bytes, stream, nullptr);
+}
+
+int fmha_mqa_fwd_sink(const void* q, const void* k, const void* v, const int32_t* kv_idx,
+                      void* out, float* lse, int B, int T, int n_h, int s_k, int hd, int pool_rows,
+                      float scale, int out_dtype, int num_splits, void* workspace,
+                      size_t workspace_bytes, void* stream, const float* sink) {
+  if (!sink) return FMHA_ERR_INVALID_ARG;
+  return fwd_impl(q, k, v, kv_idx, out, lse, B, T, n_h, s_k, hd, pool_rows, scale, out_dtype,
+                  num_splits, workspace, workspace_bytes, stream, sink);
+}
+
+int fmha_attention_sink(void* out, float* lse, const float* sink, int rows, int n_h, int hd,
+                        int out_dtype, void* stream) {
+  if (out_dtype != FMHA_F32 && out_dtype != FMHA_BF16) return FMHA_ERR_INVALID_ARG;
+  if (rows < 0 || n_h < 1 || hd < 4 || (hd % 4) != 0) return FMHA_ERR_INVALID_ARG;
+  if (rows == 0) return FMHA_OK;
+  if (!out || !lse || !sink) return FMHA_ERR_INVALID_ARG;
+  if (!aligned(out, out_dtype == FMHA_BF16 ? 8 : 16) || !aligned(lse, 4) || !aligned(sink, 4))
+    return FMHA_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return launch_status(fmha::launch_sink(out, lse, sink, rows, n_h, hd, out_dtype == FMHA_BF16,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int fmha_lse_merge(const float* o_parts, const float* lse_parts, int n_parts, int rows, int hd,

@@ -67,6 +67,25 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Attention sink (page "May 24, 2026 — Session Start Plan": a "sink merge" is
+// named, its formula is not printed; reading: one extra logit `s` per query
+// head whose value vector is zero).  Given a row's normalised output scale
+// `inv` and its log-sum-exp `lse` (natural log) over the real keys, the sink
+// joins the denominator: lse' = ln(e^lse + e^s) and O' = O e^(lse - lse').
+// s = -inf leaves the row as it is; a row without keys gets O = 0, lse' = s.
+__device__ __forceinline__ void sink_adjust(float s, float& inv, float& lse) {
+  if (s == neg_inf()) return;
+  if (lse == neg_inf()) {
+    inv = 0.f;
+    lse = s;
+    return;
+  }
+  const float hi = fmaxf(lse, s);
+  const float l2 = hi + log1pf(expf(-fabsf(lse - s)));
+  inv *= expf(lse - l2);
+  lse = l2;
+}
+
 // Key (within a 32-key block) held by accumulator register r of a lane in half
 // `hlf` of the wave (32x32 MFMA output layout).
 __device__ __forceinline__ int acc_row(int r, int hlf) { return 8 * (r >> 2) + 4 * hlf + (r & 3); }
@@ -269,11 +288,13 @@ struct Rows {
     for (int qb = 0; qb < NQB; ++qb) {
       const float lt = pair_sum(l[qb]);
       const bool empty = (m[qb] == neg_inf());
-      const float inv = empty ? 0.f : 1.f / lt;
-      const float lse_v = empty ? neg_inf() : (m[qb] + log2f(lt)) * LN2;
+      float inv = empty ? 0.f : 1.f / lt;
+      float lse_v = empty ? neg_inf() : (m[qb] + log2f(lt)) * LN2;
       const int r = row0 + qb * 32 + l32;
       if (r >= p.rows_per_group) continue;
       const int64_t row = grow0 + r;
+      if (p.sink != nullptr && p.out_mode != OUT_PARTIAL)
+        sink_adjust(p.sink[row % p.n_heads], inv, lse_v);
       const int64_t base = (p.out_mode == OUT_PARTIAL) ? (int64_t)split * p.total_rows : 0;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -315,8 +336,12 @@ struct Rows {
     for (int qb = 0; qb < NQB; ++qb) {
       const float lt = pair_sum(l[qb]);
       const bool empty = (m[qb] == neg_inf());
-      const float inv = empty ? 0.f : 1.f / lt;
-      const float lse_v = empty ? neg_inf() : (m[qb] + log2f(lt)) * LN2;
+      float inv = empty ? 0.f : 1.f / lt;
+      float lse_v = empty ? neg_inf() : (m[qb] + log2f(lt)) * LN2;
+      if (p.sink != nullptr && p.out_mode != OUT_PARTIAL) {
+        const int rs = row0 + qb * 32 + l32;
+        if (rs < p.rows_per_group) sink_adjust(p.sink[(grow0 + rs) % p.n_heads], inv, lse_v);
+      }
       char* const my = row_addr(l32);
       const int sw = l32 & swm;
 #pragma unroll

@@ -30,6 +30,9 @@ struct FwdParams {
   int num_splits;
   int out_mode;             // OutMode
   float scale_log2;         // softmax scale * log2(e)
+  const float* sink;        // optional [n_heads] sink logits (ln units); applied by
+                            // the epilogue of OUT_F32/OUT_BF16 launches only
+  int n_heads;              // head of global row g is g % n_heads
 };
 
 // Picks the tile shape for hd / rows_per_group, sets p.tiles_per_group and
@@ -45,8 +48,14 @@ int chunk_max_keys(int hd);
 hipError_t launch_chunk(FwdParams p, int hd, hipStream_t stream);
 
 // out[r] = sum_i w_i o_i[r] / sum_i w_i with w_i = exp(lse_i[r] - max_i lse_i[r]).
+// With sink (optional, [n_heads]), the sink of row r's head r % n_heads joins
+// the merged result (see sink_adjust in fmha_device.h).
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_parts,
                         int rows, int hd, void* out, bool out_bf16, float* lse,
-                        hipStream_t stream);
+                        hipStream_t stream, const float* sink = nullptr, int n_heads = 1);
+
+// In place: out[r] *= exp(lse[r] - lse'[r]), lse'[r] = ln(exp(lse[r]) + exp(sink[r % n_heads])).
+hipError_t launch_sink(void* out, float* lse, const float* sink, int rows, int n_heads, int hd,
+                       bool out_bf16, hipStream_t stream);
 
 }  // namespace fmha

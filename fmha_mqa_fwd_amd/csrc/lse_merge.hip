@@ -33,7 +33,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
                                                     const float* __restrict__ lse_parts,
                                                     int n_parts, int rows, int hd,
                                                     void* __restrict__ out,
-                                                    float* __restrict__ lse) {
+                                                    float* __restrict__ lse,
+                                                    const float* __restrict__ sink,
+                                                    int n_heads) {
   const int cpr = hd >> 2;  // 16-byte chunks per row
   const int64_t total = (int64_t)rows * cpr;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -80,32 +82,71 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
         acc *= 1.f / den;
       }
     }
+    float lse_r = (mx != -__builtin_inff()) ? mx + log2f(den) * LN2 : -__builtin_inff();
+    if (sink != nullptr) {
+      float f = 1.f;
+      dev::sink_adjust(sink[row % n_heads], f, lse_r);
+      acc *= f;
+    }
     if constexpr (OUT_BF16) {
       u32x2 w = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
       *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (int64_t)row * hd + 4 * ch) = w;
     } else {
       *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)row * hd + 4 * ch) = acc;
     }
-    if (ch == 0 && lse != nullptr)
-      lse[row] = (mx != -__builtin_inff()) ? mx + log2f(den) * LN2 : -__builtin_inff();
+    if (ch == 0 && lse != nullptr) lse[row] = lse_r;
+  }
+}
+
+// In-place attention sink on finished rows: one wave per row, lanes over the
+// row's 16-byte chunks.  Every lane reads the row's lse before lane 0 rewrites
+// it (program order within the wave), so no lane sees the updated value.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void sink_kernel(void* __restrict__ out, float* __restrict__ lse,
+                                                   const float* __restrict__ sink, int rows,
+                                                   int n_heads, int hd) {
+  const int lane = threadIdx.x & 63;
+  const int cpr = hd >> 2;
+  for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += gridDim.x * 4) {
+    float f = 1.f, l = lse[row];
+    dev::sink_adjust(sink[row % n_heads], f, l);
+    for (int ch = lane; ch < cpr; ch += 64) {
+      if constexpr (OUT_BF16) {
+        uint16_t* o = static_cast<uint16_t*>(out) + (int64_t)row * hd + 4 * ch;
+        const u32x2 w = *reinterpret_cast<const u32x2*>(o);
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          x[2 * i] = __uint_as_float(w[i] << 16) * f;
+          x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) * f;
+        }
+        *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      } else {
+        f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)row * hd + 4 * ch);
+        *o = *o * f;
+      }
+    }
+    if (lane == 0) lse[row] = l;
   }
 }
 
 template <int NP>
 void launch_np(bool out_bf16, dim3 grid, hipStream_t stream, const float* o_parts,
-               const float* lse_parts, int n_parts, int rows, int hd, void* out, float* lse) {
+               const float* lse_parts, int n_parts, int rows, int hd, void* out, float* lse,
+               const float* sink, int n_heads) {
   if (out_bf16)
     hipLaunchKernelGGL((merge_kernel<true, NP>), grid, dim3(256), 0, stream, o_parts, lse_parts,
-                       n_parts, rows, hd, out, lse);
+                       n_parts, rows, hd, out, lse, sink, n_heads);
   else
     hipLaunchKernelGGL((merge_kernel<false, NP>), grid, dim3(256), 0, stream, o_parts, lse_parts,
-                       n_parts, rows, hd, out, lse);
+                       n_parts, rows, hd, out, lse, sink, n_heads);
 }
 
 }  // namespace
 
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_parts, int rows,
-                        int hd, void* out, bool out_bf16, float* lse, hipStream_t stream) {
+                        int hd, void* out, bool out_bf16, float* lse, hipStream_t stream,
+                        const float* sink, int n_heads) {
   const int64_t total = (int64_t)rows * (hd / 4);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
@@ -114,15 +155,31 @@ hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_part
   switch (n_parts) {
 #define FMHA_MERGE_CASE(N) \
   case N:                  \
-    launch_np<N>(out_bf16, grid, stream, o_parts, lse_parts, n_parts, rows, hd, out, lse); \
+    launch_np<N>(out_bf16, grid, stream, o_parts, lse_parts, n_parts, rows, hd, out, lse, sink, \
+                 n_heads);                                                                     \
     break;
     FMHA_MERGE_CASE(1) FMHA_MERGE_CASE(2) FMHA_MERGE_CASE(3) FMHA_MERGE_CASE(4)
     FMHA_MERGE_CASE(5) FMHA_MERGE_CASE(6) FMHA_MERGE_CASE(7) FMHA_MERGE_CASE(8)
     FMHA_MERGE_CASE(12) FMHA_MERGE_CASE(16)
 #undef FMHA_MERGE_CASE
     default:
-      launch_np<0>(out_bf16, grid, stream, o_parts, lse_parts, n_parts, rows, hd, out, lse);
+      launch_np<0>(out_bf16, grid, stream, o_parts, lse_parts, n_parts, rows, hd, out, lse, sink,
+                   n_heads);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_sink(void* out, float* lse, const float* sink, int rows, int n_heads, int hd,
+                       bool out_bf16, hipStream_t stream) {
+  int64_t blocks = ((int64_t)rows + 3) / 4;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  if (out_bf16)
+    hipLaunchKernelGGL((sink_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, stream, out, lse,
+                       sink, rows, n_heads, hd);
+  else
+    hipLaunchKernelGGL((sink_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, stream, out,
+                       lse, sink, rows, n_heads, hd);
   return hipGetLastError();
 }
 

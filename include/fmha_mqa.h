@@ -88,6 +88,33 @@ int fmha_mqa_fwd(const void* q, const void* k, const void* v,
                  float scale, int out_dtype, int num_splits,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* fmha_mqa_fwd with an attention sink joined to every row (page "May 24, 2026 —
+ * Session Start Plan" names a "sink merge" — File Map, D1 Status Summary D5b —
+ * without printing it; the reading taken: one extra logit per query head whose
+ * value vector is zero).  For row (b, t, h) with lse over its keys:
+ *   lse' = ln(exp(lse) + exp(sink[h])),  out' = out * exp(lse - lse').
+ *  sink   fp32 [n_h], natural-log units like lse; -inf = no sink for that head;
+ *         must not be NULL.  4-byte aligned.
+ * Everything else as fmha_mqa_fwd.  The sink is applied once per row, in the
+ * epilogue (num_splits == 1) or in the merge (split-KV), before the output is
+ * rounded to out_dtype.  A row without keys gets out = 0, lse = sink[h]. */
+int fmha_mqa_fwd_sink(const void* q, const void* k, const void* v,
+                      const int32_t* kv_idx, void* out, float* lse,
+                      int B, int T, int n_h, int s_k, int hd, int pool_rows,
+                      float scale, int out_dtype, int num_splits,
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      const float* sink);
+
+/* The same sink applied in place to finished rows (for results already merged
+ * from several sources): for r in [0, rows), with h = r % n_h,
+ *   lse[r] <- ln(exp(lse[r]) + exp(sink[h])),  out[r, :] *= exp(lse_old - lse_new).
+ *  out   [rows, hd] of out_dtype (bf16 rows are rounded again after scaling)
+ *  lse   fp32 [rows], natural log;  sink fp32 [n_h]
+ * rows >= 0, n_h >= 1, hd >= 4 and a multiple of 4; out 16-byte aligned
+ * (8-byte for bf16), lse and sink 4-byte. */
+int fmha_attention_sink(void* out, float* lse, const float* sink, int rows,
+                        int n_h, int hd, int out_dtype, void* stream);
+
 /* Log-sum-exp merge of normalised partial results (page "CURRENT ISSUE: UMMA
  * FMHA — Full Pipeline + Production", "Next steps" 4):
  *   M = max_i lse_i,  w_i = exp(lse_i - M),

@@ -27,8 +27,9 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["fmha_lse_merge", "fmha_mqa_fwd",
-                                     "fmha_mqa_workspace_bytes", "fmha_status_string"]
+    assert _declared_functions() == ["fmha_attention_sink", "fmha_lse_merge", "fmha_mqa_fwd",
+                                     "fmha_mqa_fwd_sink", "fmha_mqa_workspace_bytes",
+                                     "fmha_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -120,3 +121,30 @@ def test_workspace_bytes(F):
 ])
 def test_merge_rejects_bad_arguments(F, args, status):
     assert F.raw_merge(*args) == status
+
+
+# ------------------------------------------------------------ attention sink
+def test_fwd_sink_requires_a_sink(F):
+    lib = F._binding._lib
+    args = (A, A, A, None, A, A, 1, 1, 1, 8, 64, 0, 0.125, 0, 1, None, 0, None)
+    assert lib.fmha_mqa_fwd_sink(*args, None) == 1
+    assert lib.fmha_mqa_fwd_sink(*args, A + 2) == 3          # misaligned sink
+    bad = (A, A, A, None, A, A, 1, 1, 1, 8, 96, 0, 0.125, 0, 1, None, 0, None)
+    assert lib.fmha_mqa_fwd_sink(*bad, A) == 2               # same checks as the plain forward
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, A, A, 4, 1, 64, 2, None), 1),       # bad dtype
+    ((A, A, A, -1, 1, 64, 0, None), 1),
+    ((A, A, A, 4, 0, 64, 0, None), 1),       # n_h < 1
+    ((A, A, A, 4, 1, 62, 0, None), 1),       # hd not a multiple of 4
+    ((None, A, A, 4, 1, 64, 0, None), 1),
+    ((A, None, A, 4, 1, 64, 0, None), 1),
+    ((A, A, None, 4, 1, 64, 0, None), 1),
+    ((A + 8, A, A, 4, 1, 64, 0, None), 3),   # fp32 out needs 16 B
+    ((A, A + 2, A, 4, 1, 64, 0, None), 3),
+    ((A, A, A + 1, 4, 1, 64, 0, None), 3),
+    ((None, None, None, 0, 1, 64, 0, None), 0),  # no rows: no-op
+])
+def test_attention_sink_validates(F, args, status):
+    assert F._binding._lib.fmha_attention_sink(*args) == status
