@@ -14,8 +14,8 @@ Contents
 Every function here is pinned by CPU tests (brute force, closed forms, library
 routines, invariants); none is "parity unpinned".
 """
-from .fp64 import (attention, attention_rows, attention_probs, lse_merge,
-                        row_metrics, split_partials, to_f64)
+from .fp64 import (attention, attention_rows, attention_probs, attention_sources,
+                   lse_merge, row_metrics, split_partials, to_f64)
 
-__all__ = ["attention", "attention_rows", "attention_probs", "lse_merge",
+__all__ = ["attention", "attention_rows", "attention_probs", "attention_sources", "lse_merge",
            "row_metrics", "split_partials", "to_f64"]

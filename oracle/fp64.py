@@ -49,7 +49,7 @@ import math
 import numpy as np
 
 __all__ = ["to_f64", "attention_rows", "attention_probs", "attention",
-           "split_partials", "lse_merge"]
+           "attention_sources", "split_partials", "lse_merge"]
 
 _CHUNK_ROWS = 2048
 
@@ -169,6 +169,46 @@ def attention(q, k, v, scale: float, kv_idx=None, rows=None,
                                     None if sink is None else sink[flat[sel] % n_h])
             O[sel] = o
             L[sel] = lse
+    if rows is None:
+        return O.reshape(B, T, n_h, dv), L.reshape(B, T, n_h)
+    return O, L
+
+
+def attention_sources(q, sources, scale: float, rows=None, sink=None):
+    """Attention of every query row over the union of several key sources.
+
+    Reading of the multi-source decode (the dsv4/kernels/cuda commit log keeps
+    a compressed KV store read through top-k row gathers and a sliding-window
+    KV store, KVCache.append_swa and gather_kv / gather_swa; their window
+    semantics are not printed): each source is ``(k, v, kv_idx)`` — dense
+    ``k, v [B, S, hd]`` with ``kv_idx None``, or pools ``[P, hd]`` with
+    ``kv_idx [B, T, S]`` — and token (b, t) attends to the concatenation of all
+    sources' keys for it, in one softmax.  Same outputs as ``attention``.
+    """
+    q = to_f64(q)
+    B, T, n_h, hd = q.shape
+    srcs = [(to_f64(k), to_f64(v), to_f64(i)) for k, v, i in sources]
+    dv = srcs[0][1].shape[-1]
+    sink = None if sink is None else to_f64(sink).reshape(-1)
+    flat = (np.arange(B * T * n_h) if rows is None
+            else np.asarray(rows, dtype=np.int64).reshape(-1))
+    O = np.empty((flat.size, dv), np.float64)
+    L = np.empty(flat.size, np.float64)
+    qf = q.reshape(B * T * n_h, hd)
+    tok = flat // n_h
+    order = np.argsort(tok, kind="stable")
+    bounds = np.flatnonzero(np.diff(tok[order])) + 1
+    for grp in np.split(order, bounds):
+        if grp.size == 0:
+            continue
+        b, t = divmod(int(tok[grp[0]]), T)
+        kv = [_kv_for_group(k, v, i, b, t) for k, v, i in srcs]
+        K = np.concatenate([x[0] for x in kv], axis=0)
+        V = np.concatenate([x[1] for x in kv], axis=0)
+        o, lse = attention_rows(qf[flat[grp]], K, V, scale,
+                                None if sink is None else sink[flat[grp] % n_h])
+        O[grp] = o
+        L[grp] = lse
     if rows is None:
         return O.reshape(B, T, n_h, dv), L.reshape(B, T, n_h)
     return O, L

@@ -418,6 +418,50 @@ def test_sink_without_keys_gives_the_sink_lse():
     assert np.all(O == 0) and L[0, 0, 0] == 1.5 and L[0, 0, 1] == -np.inf
 
 
+# ------------------------------------------------------------ several key sources
+def _two_sources(seed, B=2, T=3, n_h=2, hd=4, pool=11, s_top=5, win=3):
+    g = np.random.default_rng(seed)
+    kp = _rand((pool, hd), g)
+    vp = _rand((pool, hd), g)
+    idx = np.stack([np.stack([g.permutation(pool)[:s_top] for _ in range(T)]) for _ in range(B)])
+    kw = _rand((B, win, hd), g)
+    vw = _rand((B, win, hd), g)
+    q = _rand((B, T, n_h, hd), g)
+    return q, [(kp, vp, idx), (kw, vw, None)]
+
+
+def test_sources_match_brute_force_over_the_concatenated_keys():
+    q, src = _two_sources(3)
+    (kp, vp, idx), (kw, vw, _) = src
+    sink = np.array([0.3, -np.inf])
+    O, L = oracle.attention_sources(q, src, 0.6, sink=sink)
+    B, T = q.shape[:2]
+    for b in range(B):
+        for t in range(T):
+            keys = [list(r) for r in kp[idx[b, t]]] + [list(r) for r in kw[b]]
+            vals = [list(r) for r in vp[idx[b, t]]] + [list(r) for r in vw[b]]
+            Ob, Lb = brute.brute_attention([[_tolist(q[b, t])]], [keys], [vals], 0.6,
+                                           sink=list(sink))
+            np.testing.assert_allclose(O[b, t], np.array(Ob[0][0]), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(L[b, t], np.array(Lb[0][0]), rtol=1e-13, atol=1e-12)
+
+
+def test_sources_equal_the_merge_of_each_source():
+    """Union of sources = LSE merge of per-source results (the partition
+    identity); one source alone = plain attention."""
+    q, src = _two_sources(4, hd=6)
+    O, L = oracle.attention_sources(q, src, 0.5)
+    parts = [oracle.attention(q, k, v, 0.5, kv_idx=i) for k, v, i in src]
+    Om, Lm = oracle.lse_merge(np.stack([p[0].reshape(-1, 6) for p in parts]),
+                              np.stack([p[1].reshape(-1) for p in parts]))
+    np.testing.assert_allclose(O.reshape(-1, 6), Om, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L.reshape(-1), Lm, rtol=1e-13, atol=1e-12)
+    O1, L1 = oracle.attention_sources(q, src[1:], 0.5)
+    O2, L2 = oracle.attention(q, src[1][0], src[1][1], 0.5)
+    np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(L1, L2, rtol=0, atol=1e-13)
+
+
 def _sink_pin():
     test_sink_matches_brute_force(1, 2, 3, 4, 3)
     test_sink_is_an_extra_key_with_zero_value()
