@@ -176,6 +176,45 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    sink)()
 
 
+def fwd_sources(q: torch.Tensor, sources, scale: Optional[float] = None,
+                out_dtype: torch.dtype = torch.bfloat16, sink: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention over the union of several key sources, e.g. top-k rows
+    gathered from a compressed pool plus a dense sliding window.
+
+    sources: sequence of (k, v, kv_idx, num_splits) — dense k, v [B, S, hd]
+    with kv_idx None, or pools [P, hd] with kv_idx [B, T, S]; num_splits as
+    for fwd.  Each source runs through fmha_mqa_fwd into fp32 partials, which
+    fmha_lse_merge combines; the sink (fp32 [n_h]) joins once, after the
+    merge (fmha_attention_sink).  Returns (out [B, T, n_h, hd], lse [B, T, n_h]).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, n_h, hd]")
+    B, T, n_h, hd = q.shape
+    n = len(sources)
+    if n < 1:
+        raise ValueError("at least one key source is needed")
+    dev = q.device
+    rows = B * T * n_h
+    parts = torch.empty((n, B, T, n_h, hd), dtype=torch.float32, device=dev)
+    lse_parts = torch.empty((n, B, T, n_h), dtype=torch.float32, device=dev)
+    for i, src in enumerate(sources):
+        k, v, kv_idx = src[0], src[1], src[2]
+        splits = src[3] if len(src) > 3 else 1
+        fwd(q, k, v, kv_idx, scale, torch.float32, splits, out=parts[i], lse=lse_parts[i],
+            stream=stream)
+    if out is None:
+        out = torch.empty((B, T, n_h, hd), dtype=out_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, T, n_h), dtype=torch.float32, device=dev)
+    lse_merge(parts.view(n, rows, hd), lse_parts.view(n, rows), out.dtype,
+              out=out.view(rows, hd), lse=lse.view(rows), stream=stream)
+    if sink is not None:
+        apply_sink(out, lse, sink, stream=stream)
+    return out, lse
+
+
 def apply_sink(out: torch.Tensor, lse: torch.Tensor, sink: torch.Tensor, stream=None
                ) -> Tuple[torch.Tensor, torch.Tensor]:
     """fmha_attention_sink in place: out [..., n_h, hd] (fp32 or bf16) and lse
