@@ -43,7 +43,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* kv_idx,
              void* stream, const float* sink) {
   if (out_dtype != FMHA_F32 && out_dtype != FMHA_BF16) return FMHA_ERR_INVALID_ARG;
   if (B < 0 || T < 0 || n_h < 0 || s_k < 0 || num_splits < 1) return FMHA_ERR_INVALID_ARG;
-  if (hd != 64 && hd != 128 && hd != 256) return FMHA_ERR_UNSUPPORTED;
+  if (hd != 64 && hd != 128 && hd != 256 && hd != 512) return FMHA_ERR_UNSUPPORTED;
   if (!(scale > 0.f) || !isfinite(scale)) return FMHA_ERR_INVALID_ARG;
   const int64_t rows = (int64_t)B * T * n_h;
   if (rows == 0) return FMHA_OK;  // nothing to compute

@@ -90,8 +90,10 @@ __device__ __forceinline__ void sink_adjust(float s, float& inv, float& lse) {
 // `hlf` of the wave (32x32 MFMA output layout).
 __device__ __forceinline__ int acc_row(int r, int hlf) { return 8 * (r >> 2) + 4 * hlf + (r & 3); }
 
-// Per-wave state of QW query rows (NQB = QW/32 column blocks).
-template <int HD, int QW>
+// Per-wave state of QW query rows (NQB = QW/32 column blocks) over HD of the
+// head dim; LD is the row length of q and of the output (HD, or the full head
+// dim when several waves share the rows and each holds a column range).
+template <int HD, int QW, int LD = HD>
 struct Rows {
   static constexpr int NQB = QW / 32;
   static constexpr int NDS = HD / 16;  // 16-wide contraction steps of QK^T
@@ -102,14 +104,14 @@ struct Rows {
   float l[NQB];                        // this lane-half's running row sum
   float alpha[NQB];                    // last rescale factor
 
-  // Lane (hlf, l32) of block qb holds q[row l32][16*ds + 8*hlf .. +7].
+  // Lane (hlf, l32) of block qb holds q[row l32][col0 + 16*ds + 8*hlf .. +7].
   __device__ __forceinline__ void load_q(const uint16_t* q, int64_t grow0, int row0,
-                                         int rows_in_group, int l32, int hlf) {
+                                         int rows_in_group, int l32, int hlf, int col0 = 0) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int r = row0 + qb * 32 + l32;
       const bool ok = r < rows_in_group;
-      const uint16_t* qrow = q + (grow0 + (ok ? r : 0)) * HD + 8 * hlf;
+      const uint16_t* qrow = q + (grow0 + (ok ? r : 0)) * LD + col0 + 8 * hlf;
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         u32x4 w = {0u, 0u, 0u, 0u};
@@ -282,8 +284,11 @@ struct Rows {
   // lse = -inf.  OUT_PARTIAL writes fp32 to plane `split` of [splits, rows, HD].
   // Direct form: each lane stores its own 4-element pieces (a row's 32-wide d
   // block arrives as 8 pieces from 2 lanes per instruction).
+  // col0: first output column this wave holds; write_lse: this wave writes
+  // the rows' lse (one wave per row when several share it).
   __device__ __forceinline__ void store(const FwdParams& p, int64_t grow0, int row0, int split,
-                                        int l32, int hlf) const {
+                                        int l32, int hlf, int col0 = 0,
+                                        bool write_lse = true) const {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const float lt = pair_sum(l[qb]);
@@ -306,13 +311,14 @@ struct Rows {
           for (int i = 0; i < 4; ++i) val[i] = o[db][qb][4 * rg + i] * inv;
           if (p.out_mode == OUT_BF16) {
             u32x2 w = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row * HD + d) = w;
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row * LD + col0 + d) = w;
           } else {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + (base + row) * HD + d) = val;
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + (base + row) * LD + col0 + d) =
+                val;
           }
         }
       }
-      if (hlf == 0) p.lse[base + row] = lse_v;
+      if (hlf == 0 && write_lse) p.lse[base + row] = lse_v;
     }
   }
 
@@ -323,11 +329,14 @@ struct Rows {
   // (0..31), holding at least HD*4 bytes; only this wave touches it.
   template <class RowAddr>
   __device__ __forceinline__ void store_lds(const FwdParams& p, int64_t grow0, int row0, int split,
-                                            int lane, RowAddr row_addr) const {
+                                            int lane, RowAddr row_addr, int col0 = 0,
+                                            bool write_lse = true) const {
     const int l32 = lane & 31;
     const int hlf = lane >> 5;
     const bool bf = (p.out_mode == OUT_BF16);
-    const int rb = HD * (bf ? 2 : 4);   // output bytes per row
+    const int esz = bf ? 2 : 4;
+    const int rb = HD * esz;            // bytes of a row this wave holds
+    const int64_t grb = (int64_t)LD * esz;  // bytes of a whole output row
     const int cpr = rb / 16;            // 16-byte chunks per row (8 .. 64)
     const int swm = cpr >= 16 ? 15 : 7;
     const int64_t base = (p.out_mode == OUT_PARTIAL) ? (int64_t)split * p.total_rows : 0;
@@ -369,10 +378,10 @@ struct Rows {
         const u32x4 v = *reinterpret_cast<const u32x4*>(row_addr(r) + 16 * (ch ^ (r & swm)));
         const int rr = row0 + qb * 32 + r;
         if (rr < p.rows_per_group)
-          *reinterpret_cast<u32x4*>(out + (base + grow0 + rr) * rb + 16 * ch) = v;
+          *reinterpret_cast<u32x4*>(out + (base + grow0 + rr) * grb + col0 * esz + 16 * ch) = v;
       }
       const int r = row0 + qb * 32 + l32;
-      if (hlf == 0 && r < p.rows_per_group) p.lse[base + grow0 + r] = lse_v;
+      if (hlf == 0 && write_lse && r < p.rows_per_group) p.lse[base + grow0 + r] = lse_v;
       __builtin_amdgcn_wave_barrier();  // LDS reads done before the next block's writes
     }
   }

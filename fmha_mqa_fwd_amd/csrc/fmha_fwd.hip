@@ -56,6 +56,16 @@ struct Lds {
 
 constexpr uint32_t OOB = 0x80000000u;  // beyond any descriptor's byte count
 
+// Head dims above 256: DSPLIT = 2 waves share the same QW rows, each holding
+// half of the head dim (its Q^T columns, its O^T rows): each computes a
+// partial S over its half, the two partials are summed through LDS (the
+// softmax needs the whole contraction first), both run the same softmax and
+// each does PV for its half.
+template <int HD>
+struct DSplit {
+  static constexpr int value = HD > 256 ? 2 : 1;
+};
+
 template <int HD, int QW, int KT, int WAVES, bool GATHER, int WPE>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(FwdParams p) {
@@ -63,7 +73,10 @@ void fwd_kernel(FwdParams p) {
   constexpr int NQB = QW / 32;
   constexpr int NKB = KT / 32;   // 32-key row blocks of S^T per tile
   constexpr int NKS = KT / 16;   // 16-key contraction steps of PV per tile
-  constexpr int M_WG = WAVES * QW;
+  constexpr int DSPLIT = DSplit<HD>::value;
+  constexpr int HDW = HD / DSPLIT;  // head-dim columns one wave holds
+  constexpr int M_WG = WAVES / DSPLIT * QW;
+  static_assert(DSPLIT == 1 || (NQB == 1 && NKB == 1), "split head dim: one S block per wave");
   constexpr int ROW = Lds<HD>::ROW;
   constexpr int KS = Lds<HD>::K_STRIDE;
   constexpr int VS = Lds<HD>::V_STRIDE;
@@ -78,6 +91,8 @@ void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char sV0[NVI * 1024], sV1[NVI * 1024];
   __shared__ int sIdx[GATHER ? 3 : 1][KT];    // gather: pool rows of a tile (-1 = masked)
   __shared__ int sValid[GATHER ? 2 : 1][KT];  // gather: key usable, per K buffer
+  // split head dim: each wave's partial S^T (16 floats per lane)
+  __shared__ __attribute__((aligned(16))) float sX[DSPLIT > 1 ? WAVES * 64 * 16 : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,7 +109,9 @@ void fwd_kernel(FwdParams p) {
   const int key_lo = split * p.chunk;
   const int key_hi = min(key_lo + p.chunk, p.s_k);
   const int n_tiles = key_hi > key_lo ? (key_hi - key_lo + KT - 1) / KT : 0;
-  const int row0 = tile * M_WG + wave * QW;  // first row of this wave in its group
+  const int dh = wave % DSPLIT;              // which head-dim part this wave holds
+  const int col0 = dh * HDW;
+  const int row0 = tile * M_WG + wave / DSPLIT * QW;  // first row of this wave in its group
   const int64_t grow0 = (int64_t)group * p.rows_per_group;
   const uint16_t* kbase = GATHER ? p.k : p.k + (int64_t)group * p.s_k * HD;
   const uint16_t* vbase = GATHER ? p.v : p.v + (int64_t)group * p.s_k * HD;
@@ -183,8 +200,8 @@ void fwd_kernel(FwdParams p) {
     }
   };
 
-  Rows<HD, QW> w;
-  w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf);
+  Rows<HDW, QW, HD> w;
+  w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf, col0);
   const float c = p.scale_log2;
 
   // Per-lane LDS byte offsets of the MFMA operands within a tile buffer.
@@ -196,8 +213,8 @@ void fwd_kernel(FwdParams p) {
   //  which is where S^T's accumulator layout put that lane's P values.
   const int jj = lane & 15;
   const int dsub = (lane >> 4) & 1;
-  const int k_lane = l32 * KS + 16 * hlf;
-  const int v_lane = (4 * hlf + (jj >> 2)) * VS + 2 * (16 * dsub + 4 * (jj & 3));
+  const int k_lane = l32 * KS + 16 * hlf + 2 * col0;
+  const int v_lane = (4 * hlf + (jj >> 2)) * VS + 2 * (16 * dsub + 4 * (jj & 3)) + 2 * col0;
 
   // One tile: compute tile t from (kcur, vcur) while tile t+1 streams into
   // (knext, vnext).  Buffers are distinct LDS objects in each unrolled copy.
@@ -221,6 +238,24 @@ void fwd_kernel(FwdParams p) {
     w.template qk<NKB>(s, [&](int kb, int ds) {
       return *reinterpret_cast<const bf16x8*>(kcur + k_lane + kb * 32 * KS + ds * 32);
     });
+    if constexpr (DSPLIT == 2) {
+      // S^T = this wave's partial + its partner's (same lanes, same layout)
+      f32x4* mine = reinterpret_cast<f32x4*>(sX + (wave * 64 + lane) * 16);
+      const f32x4* theirs = reinterpret_cast<const f32x4*>(sX + ((wave ^ 1) * 64 + lane) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        mine[i] = f32x4{s[0][0][4 * i], s[0][0][4 * i + 1], s[0][0][4 * i + 2], s[0][0][4 * i + 3]};
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the partial is in LDS
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 o = theirs[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[0][0][4 * i + e] += o[e];
+      }
+    }
     bool masked = !GATHER && (t0 + KT > key_hi);
     if constexpr (GATHER) masked = __any(lane < KT && !sValid[vb][lane & (KT - 1)]);
     if (masked) {
@@ -269,21 +304,23 @@ void fwd_kernel(FwdParams p) {
   // Epilogue through LDS when this workgroup's output rows fit in the K tile
   // buffers (bf16 outputs), else each lane stores its own pieces.  The last
   // barrier of the loop has retired every read of those buffers.
-  constexpr int RB_BF16 = HD * 2;
+  constexpr int RB_BF16 = HDW * 2;
   constexpr int STAGE_BYTES = NKI * 1024;
   static_assert(QW == 32, "epilogue staging assumes 32 rows per wave");
   if constexpr (WAVES == 4 && 2 * QW * RB_BF16 <= STAGE_BYTES) {
     if (p.out_mode == OUT_BF16) {
       char* const region = (wave < 2 ? sK0 : sK1) + (wave & 1) * QW * RB_BF16;
-      w.store_lds(p, grow0, row0, split, lane, [&](int r) { return region + r * RB_BF16; });
+      w.store_lds(p, grow0, row0, split, lane, [&](int r) { return region + r * RB_BF16; }, col0,
+                  dh == 0);
       return;
     }
   }
-  w.store(p, grow0, row0, split, l32, hlf);
+  w.store(p, grow0, row0, split, l32, hlf, col0, dh == 0);
 }
 
 struct Shape {
   int qw, kt, waves, wpe;
+  int rows() const { return waves * qw; }  // rows per workgroup (before a head-dim split)
 };
 
 // 32 rows per wave keeps a wave within 170 (dense, 32-key tiles: three waves
@@ -291,6 +328,7 @@ struct Shape {
 // one wave's softmax overlaps other waves' MFMAs.  hd 256 needs the whole
 // register file: one wave per SIMD.
 Shape pick_shape(int hd, bool gather) {
+  if (hd > 256) return {32, 32, 2, 1};  // 2 row blocks x 2 head-dim halves = 4 waves
   if (hd >= 256) return {32, 32, 4, 1};
   if (gather) return {32, 64, 4, 2};
   return {32, 32, 4, 3};
@@ -304,21 +342,27 @@ hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// a split whose keys fit in LDS whole goes to the whole-chunk kernel
+bool use_chunk(const FwdParams& p, int hd) {
+  const int mk = chunk_max_keys(hd);
+  return mk > 0 && p.chunk <= mk;
+}
+
 }  // namespace
 
 int64_t fwd_grid_size(const FwdParams& p, int hd) {
   const Shape sh = pick_shape(hd, p.kv_idx != nullptr);
-  const int64_t m_wg = (p.chunk <= chunk_max_keys(hd)) ? 128 : (int64_t)sh.waves * sh.qw;
+  const int64_t m_wg = use_chunk(p, hd) ? 128 : (int64_t)sh.rows();
   const int64_t tiles = (p.rows_per_group + m_wg - 1) / m_wg;
   return tiles * p.n_groups * p.num_splits;
 }
 
 hipError_t launch_fwd(FwdParams p, int hd, hipStream_t stream) {
   // a split that fits in LDS whole is staged at once (decode shapes)
-  if (p.chunk <= chunk_max_keys(hd)) return launch_chunk(p, hd, stream);
+  if (use_chunk(p, hd)) return launch_chunk(p, hd, stream);
   const bool gather = p.kv_idx != nullptr;
   const Shape sh = pick_shape(hd, gather);
-  const int m_wg = sh.waves * sh.qw;
+  const int m_wg = sh.rows();
   p.tiles_per_group = (p.rows_per_group + m_wg - 1) / m_wg;
   switch (hd) {
     case 64:
@@ -330,6 +374,9 @@ hipError_t launch_fwd(FwdParams p, int hd, hipStream_t stream) {
     case 256:
       return gather ? launch_t<256, 32, 32, 4, 1, true>(p, stream)
                     : launch_t<256, 32, 32, 4, 1, false>(p, stream);
+    case 512:
+      return gather ? launch_t<512, 32, 32, 4, 1, true>(p, stream)
+                    : launch_t<512, 32, 32, 4, 1, false>(p, stream);
     default:
       return hipErrorInvalidValue;
   }

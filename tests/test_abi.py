@@ -78,7 +78,7 @@ def test_status_strings(F):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(hd=96), 2), (dict(hd=512), 2), (dict(hd=0), 2),
+    (dict(hd=96), 2), (dict(hd=1024), 2), (dict(hd=0), 2),
     (dict(out_dtype=2), 1), (dict(B=-1), 1), (dict(s_k=-1), 1), (dict(num_splits=0), 1),
     (dict(num_splits=9), 1), (dict(scale=0.0), 1), (dict(scale=-1.0), 1),
     (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),

@@ -87,14 +87,14 @@ def test_sparse_topk_full_size_sampled(F):
 
 
 # ------------------------------------------------------------------ sweeps
-@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
 @pytest.mark.parametrize("s_k", [1, 7, 64, 129, 256, 1000])
 def test_head_dim_and_key_count_sweep(F, hd, s_k):
     w = W.make_custom(B=2, T=3, n_h=37, hd=hd, s_k=s_k, out_dtype="f32", seed=hd * 7 + s_k)
     _case(F, w)
 
 
-@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
 @pytest.mark.parametrize("rows", [(1, 1, 1), (1, 129, 2), (3, 5, 64), (1, 2, 200), (2, 1, 300)])
 def test_ragged_row_counts(F, hd, rows):
     B, T, n_h = rows
@@ -265,6 +265,27 @@ def test_plan_relaunches_on_the_same_tensors(F):
     out, lse = plan()
     torch.cuda.synchronize()
     _check(out, lse, q, k, v2, None, w.scale)
+
+
+# ------------------------------------------------------------ head dim 512
+# DeepSeek-V4's head dim (page "May 24, 2026 — Session Start Plan", File Map:
+# config hd=512; Key Numbers: Flash n_h 64 / top_k 512, Pro n_h 128 / top_k 1024).
+def test_hd512_pro_decode_split(F):
+    w = W.make_custom(B=4, T=1, n_h=128, hd=512, s_k=1024, out_dtype="bf16", num_splits=8,
+                      seed=512)
+    _case(F, w)
+
+
+def test_hd512_flash_sparse_topk(F):
+    w = W.make_custom(B=2, T=16, n_h=64, hd=512, s_k=512, pool=8192, out_dtype="bf16", seed=513)
+    _case(F, w, rows=_sample_rows(w.rows, 640, 6))
+
+
+@pytest.mark.parametrize("splits,out_dtype", [(1, "f32"), (3, "f32"), (2, "bf16")])
+def test_hd512_dense_prefill(F, splits, out_dtype):
+    w = W.make_custom(B=1, T=40, n_h=8, hd=512, s_k=700, out_dtype=out_dtype, num_splits=splits,
+                      seed=514 + splits)
+    _case(F, w)
 
 
 # --------------------------------------------------------------- the merge
