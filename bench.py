@@ -97,11 +97,15 @@ COPY_BYTES = 256 << 20   # calibration copy: reads and writes this many bytes
 
 
 class Case:
-    def __init__(self, cid, dev):
+    """One workload's inputs and outputs resident on the GPU; calling it
+    launches the forward once.  `wl` is a config id or a Workload; `sink`
+    optionally joins an attention sink of that many heads."""
+
+    def __init__(self, wl, dev, sink=False):
         import fmha_mqa_fwd_amd as F
 
         self.F = F
-        self.w = W.get(cid)
+        self.w = W.get(wl) if isinstance(wl, int) else wl
         q, k, v, idx = W.make_inputs(self.w)
         self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
         self.idx = None if idx is None else idx.to(dev)
@@ -111,13 +115,64 @@ class Case:
         self.lse = torch.empty((w.B, w.T, w.n_h), dtype=torch.float32, device=dev)
         nb = F.workspace_bytes(w.B, w.T, w.n_h, w.hd, w.num_splits)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        self.sink = None
+        if sink:
+            g = torch.Generator().manual_seed(7)
+            self.sink = (torch.randn(w.n_h, generator=g) * 2.0).to(dev)
         # arguments marshalled once: a timed call is the C launch itself
         self.plan = F.FwdPlan(self.q, self.k, self.v, self.idx, scale=w.scale,
                               out_dtype=self.out_dtype, num_splits=w.num_splits,
-                              out=self.out, lse=self.lse, workspace=self.ws)
+                              out=self.out, lse=self.lse, workspace=self.ws, sink=self.sink)
 
     def __call__(self):
         self.plan()
+
+
+class SourcesCase:
+    """Decode over two key sources — top-k rows gathered from a compressed
+    pool plus a dense sliding window — in one softmax: one forward per source
+    into fp32 partials, then the LSE merge (the composition fwd_sources runs),
+    with every launch's arguments marshalled once."""
+
+    def __init__(self, dev, B=32, n_h=64, hd=512, top_k=512, pool=32768, window=128):
+        import fmha_mqa_fwd_amd as F
+
+        top = W.make_custom(B=B, T=1, n_h=n_h, hd=hd, s_k=top_k, pool=pool, out_dtype="bf16",
+                            seed=3001, name="topk_source")
+        win = W.make_custom(B=B, T=1, n_h=1, hd=hd, s_k=window, out_dtype="bf16", seed=3002,
+                            name="window_source")
+        q, kp, vp, idx = W.make_inputs(top)
+        _, kw, vw, _ = W.make_inputs(win)
+        self.q, kp, vp, idx, kw, vw = (t.to(dev) for t in (q, kp, vp, idx, kw, vw))
+        self._keep = (kp, vp, idx, kw, vw)
+        rows = B * n_h
+        self.parts = torch.empty((2, B, 1, n_h, hd), dtype=torch.float32, device=dev)
+        self.lse_parts = torch.empty((2, B, 1, n_h), dtype=torch.float32, device=dev)
+        self.out = torch.empty((B, 1, n_h, hd), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, 1, n_h), dtype=torch.float32, device=dev)
+        self.plans = [F.FwdPlan(self.q, kp, vp, idx, scale=top.scale, out_dtype=torch.float32,
+                                out=self.parts[0], lse=self.lse_parts[0]),
+                      F.FwdPlan(self.q, kw, vw, None, scale=top.scale, out_dtype=torch.float32,
+                                out=self.parts[1], lse=self.lse_parts[1])]
+        lib = F._binding._lib
+        self._merge = lib.fmha_lse_merge
+        self._margs = (self.parts.data_ptr(), self.lse_parts.data_ptr(), 2, rows, hd,
+                       self.out.data_ptr(), F.FMHA_BF16, self.lse.data_ptr(),
+                       torch.cuda.current_stream().cuda_stream)
+        # bytes the method must move once: Q, gathered top-k K/V rows (+ idx),
+        # window K/V, bf16 O and lse
+        self.bytes = (rows * hd * 2 + 2 * B * top_k * hd * 2 + B * top_k * 4
+                      + 2 * B * window * hd * 2 + rows * hd * 2 + rows * 4)
+        self.flops = 4 * rows * (top_k + window) * hd
+        self.desc = (f"decode over two sources: B={B} T=1 n_h={n_h} hd={hd}, top-k {top_k} of "
+                     f"{pool} pool rows + {window}-key window, bf16 out")
+
+    def __call__(self):
+        for plan in self.plans:
+            plan()
+        st = self._merge(*self._margs)
+        if st != 0:
+            raise RuntimeError(f"fmha_lse_merge failed: status {st}")
 
 
 def time_case(case, steps, warmup, flush_buf):
@@ -423,6 +478,37 @@ def main():
         del case
         torch.cuda.empty_cache()
 
+    # the widened rows: head dim 512 (decode split and Flash top-k), the
+    # attention sink fused into decode, attention over two key sources
+    nxt = {}
+    nxt_cases = (
+        ("hd512_decode", lambda: Case(W.make_custom(B=32, T=1, n_h=128, hd=512, s_k=1024,
+                                                    out_dtype="bf16", num_splits=8, seed=2001,
+                                                    name="hd512_decode"), dev)),
+        ("hd512_flash_topk", lambda: Case(W.make_custom(B=4, T=512, n_h=64, hd=512, s_k=512,
+                                                        pool=32768, out_dtype="bf16", seed=2002,
+                                                        name="hd512_flash_topk"), dev)),
+        ("decode_sink", lambda: Case(3, dev, sink=True)),
+        ("two_source_decode", lambda: SourcesCase(dev)),
+    )
+    for name, make in nxt_cases:
+        case = make()
+        t = time_case(case, args.steps, args.warmup, flush_buf)
+        if isinstance(case, SourcesCase):
+            flops, nbytes, desc = case.flops, case.bytes, case.desc
+        else:
+            flops, nbytes, desc = case.w.flops, case.w.algorithmic_bytes(), case.w.describe()
+        ent = {"us_per_call": round(t["ms"] * 1e3, 2), "us_per_call_warm": round(t["ms_warm"] * 1e3, 2),
+               "TFLOPs": round(flops / (t["ms"] * 1e-3) / 1e12, 2),
+               "GBps": round(nbytes / (t["ms"] * 1e-3) / 1e9, 1), "workload": desc}
+        ent["frac_of_mfma_peak"] = round(ent["TFLOPs"] / PEAK_BF16_TFLOPS, 4)
+        ent["frac_of_hbm_peak"] = round(ent["GBps"] / PEAK_HBM_GBPS, 4)
+        nxt[name] = ent
+        print(f"[bench] {name}: {ent['us_per_call']:.1f} us/call flushed, {ent['TFLOPs']:.1f} "
+              f"TFLOP/s, {ent['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+        del case
+        torch.cuda.empty_cache()
+
     copy_gbps = copy_ceiling(dev)
     print(f"[bench] device copy: {copy_gbps:.0f} GB/s (read + write)", file=sys.stderr, flush=True)
 
@@ -467,6 +553,7 @@ def main():
                            "us_per_call_warm": round(p["ms_warm"] * 1e3, 2),
                            **committed_kernel_stats("mqa_prefill")},
     }
+    line["next"] = nxt
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
