@@ -10,12 +10,16 @@ Contents
     only to bound memory (no tiling, no online rescale, no fusion).
   * ``oracle.brute``     — the same definition as scalar pure-Python loops with
     ``math.fsum``; used on tiny shapes to pin ``oracle.fp64``.
+  * ``oracle.indexer``   — top-k indexer scores (float64) and the exact top-k
+    selection that produce gather lists.
 
 Every function here is pinned by CPU tests (brute force, closed forms, library
 routines, invariants); none is "parity unpinned".
 """
 from .fp64 import (attention, attention_rows, attention_probs, attention_sources,
                    lse_merge, row_metrics, split_partials, to_f64)
+from .indexer import index_scores, topk_select
 
 __all__ = ["attention", "attention_rows", "attention_probs", "attention_sources", "lse_merge",
+           "index_scores", "topk_select",
            "row_metrics", "split_partials", "to_f64"]
