@@ -34,6 +34,9 @@ SIGNATURES = {
                                      _c_int, _c_void_p]),
     "fmha_lse_merge": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
                                 _c_int, _c_void_p, _c_void_p]),
+    "fmha_index_scores": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                   _c_int, _c_int, _c_int, _c_void_p]),
+    "fmha_topk_select": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p]),
     "fmha_status_string": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -255,6 +258,50 @@ def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
     if st != 0:
         raise FmhaError("fmha_lse_merge", st)
     return out, lse
+
+
+def index_scores(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor,
+                 scores: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fmha_index_scores: q bf16 [B, T, H, c], k bf16 [P, c], w fp32 [B, T, H]
+    -> scores fp32 [B, T, P]."""
+    if q.dim() != 4 or k.dim() != 2 or k.shape[1] != q.shape[3] or w.shape != q.shape[:3]:
+        raise ValueError("q must be [B, T, H, c], k [P, c] and w [B, T, H]")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or w.dtype != torch.float32:
+        raise ValueError("q and k must be bfloat16, w float32")
+    if not (q.is_contiguous() and k.is_contiguous() and w.is_contiguous()):
+        raise ValueError("q, k and w must be contiguous")
+    B, T, H, c = q.shape
+    P = k.shape[0]
+    if scores is None:
+        scores = torch.empty((B, T, P), dtype=torch.float32, device=q.device)
+    st = _lib.fmha_index_scores(_ptr(q), _ptr(k), _ptr(w), _ptr(scores), B, T, H, c, P,
+                                _stream_handle(stream))
+    if st != 0:
+        raise FmhaError("fmha_index_scores", st)
+    return scores
+
+
+def topk_select(scores: torch.Tensor, top_k: int, idx: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """fmha_topk_select over the last dim of fp32 scores [..., P] -> int32
+    [..., top_k] (ascending ids, -1 padding)."""
+    if scores.dtype != torch.float32 or not scores.is_contiguous():
+        raise ValueError("scores must be contiguous float32")
+    P = scores.shape[-1]
+    rows = scores.numel() // P if P else 0
+    if idx is None:
+        idx = torch.empty((*scores.shape[:-1], top_k), dtype=torch.int32, device=scores.device)
+    st = _lib.fmha_topk_select(_ptr(scores), _ptr(idx), rows, P, int(top_k),
+                               _stream_handle(stream))
+    if st != 0:
+        raise FmhaError("fmha_topk_select", st)
+    return idx
+
+
+def indexer_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, top_k: int,
+                 stream=None) -> torch.Tensor:
+    """kv_idx int32 [B, T, top_k] for fwd: the index scores, then the top-k."""
+    return topk_select(index_scores(q, k, w, stream=stream), top_k, stream=stream)
 
 
 def raw_fwd(*args) -> int:

@@ -1,6 +1,8 @@
 """Builds libfmha_mqa.so in-tree for gfx950 with hipcc.
 
-    python -m fmha_mqa_fwd_amd.build        (or __graft_entry__.build())
+    python fmha_mqa_fwd_amd/build.py        (or __graft_entry__.build())
+
+(run by path: importing the package loads the library this builds).
 
 Each translation unit is compiled to an object in parallel, then linked into
 ``fmha_mqa_fwd_amd/libfmha_mqa.so``.  The library is written to a temporary
@@ -21,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libfmha_mqa.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["api.hip", "fmha_fwd.hip", "fmha_chunk.hip", "lse_merge.hip"]
+SOURCES = ["api.hip", "fmha_fwd.hip", "fmha_chunk.hip", "lse_merge.hip", "fmha_indexer.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are kept out of the generated code on purpose; the

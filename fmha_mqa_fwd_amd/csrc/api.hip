@@ -150,6 +150,34 @@ int fmha_attention_sink(void* out, float* lse, const float* sink, int rows, int 
                                          static_cast<hipStream_t>(stream)));
 }
 
+int fmha_index_scores(const void* q, const void* k, const float* w, float* scores, int B, int T,
+                      int n_ih, int c, int P, void* stream) {
+  if (B < 0 || T < 0 || P < 1) return FMHA_ERR_INVALID_ARG;
+  if ((n_ih != 32 && n_ih != 64) || (c != 64 && c != 128)) return FMHA_ERR_UNSUPPORTED;
+  const int64_t tokens = (int64_t)B * T;
+  if (tokens == 0) return FMHA_OK;
+  if (tokens > INT32_MAX || (int64_t)P * c * 2 > INT32_MAX) return FMHA_ERR_UNSUPPORTED;
+  if (!q || !k || !w || !scores) return FMHA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(scores, 4))
+    return FMHA_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return launch_status(fmha::launch_index_scores(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), w, scores, (int)tokens,
+      n_ih, c, P, static_cast<hipStream_t>(stream)));
+}
+
+int fmha_topk_select(const float* scores, int32_t* idx, int rows, int P, int top_k,
+                     void* stream) {
+  if (rows < 0 || P < 1 || top_k < 1) return FMHA_ERR_INVALID_ARG;
+  if (P > fmha::topk_max_pool()) return FMHA_ERR_UNSUPPORTED;
+  if (rows == 0) return FMHA_OK;
+  if (!scores || !idx) return FMHA_ERR_INVALID_ARG;
+  if (!aligned(scores, 4) || !aligned(idx, 4)) return FMHA_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return launch_status(
+      fmha::launch_topk(scores, idx, rows, P, top_k, static_cast<hipStream_t>(stream)));
+}
+
 int fmha_lse_merge(const float* o_parts, const float* lse_parts, int n_parts, int rows, int hd,
                    void* out, int out_dtype, float* lse, void* stream) {
   if (out_dtype != FMHA_F32 && out_dtype != FMHA_BF16) return FMHA_ERR_INVALID_ARG;

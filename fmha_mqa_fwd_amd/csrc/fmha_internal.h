@@ -58,4 +58,15 @@ hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_part
 hipError_t launch_sink(void* out, float* lse, const float* sink, int rows, int n_heads, int hd,
                        bool out_bf16, hipStream_t stream);
 
+// Top-k indexer: scores [tokens, P] fp32 from q bf16 [tokens, H, C], k bf16
+// [P, C], w fp32 [tokens, H] (H in {32, 64}, C in {64, 128}); selection of the
+// top_k largest scores of each row (P <= topk_max_pool()) into idx int32
+// [rows, top_k], ascending entry ids, -1 padding.
+hipError_t launch_index_scores(const uint16_t* q, const uint16_t* k, const float* w,
+                               float* scores, int tokens, int H, int C, int P,
+                               hipStream_t stream);
+int topk_max_pool();
+hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int P, int top_k,
+                       hipStream_t stream);
+
 }  // namespace fmha

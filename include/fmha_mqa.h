@@ -130,6 +130,27 @@ int fmha_lse_merge(const float* o_parts, const float* lse_parts, int n_parts,
                    int rows, int hd, void* out, int out_dtype, float* lse,
                    void* stream);
 
+/* Index scores of the top-k indexer that produces kv_idx (the dsv4/kernels/cuda
+ * commit log, indexer_score_topk: per-head scores with per-head weights, the
+ * 1024 best pool entries kept per token; the formula is not printed — reading:
+ * the DeepSeek sparse-attention indexer form, one index key per entry):
+ *   scores[b, t, s] = sum_h w[b, t, h] * max(0, sum_c q[b, t, h, c] * k[s, c])
+ *  q       bf16 [B, T, n_ih, c] index queries;  k  bf16 [P, c] index keys
+ *  w       fp32 [B, T, n_ih] head weights;      scores  fp32 [B, T, P] (written)
+ * n_ih in {32, 64} and c in {64, 128} (else FMHA_ERR_UNSUPPORTED); B, T >= 0;
+ * P >= 1 with P*c*2 < 2^31.  q, k 16-byte aligned; w, scores 4-byte. */
+int fmha_index_scores(const void* q, const void* k, const float* w, float* scores,
+                      int B, int T, int n_ih, int c, int P, void* stream);
+
+/* Exact top-k of each row of scores fp32 [rows, P] (the selection of the same
+ * indexer): idx int32 [rows, top_k] receives the ids of the top_k largest
+ * scores, ties broken towards the smaller id, in ascending id order; when
+ * P < top_k the list is padded with -1 (a key the attention masks).
+ * rows >= 0, 1 <= P <= 32768 (a row is selected in LDS; larger P gives
+ * FMHA_ERR_UNSUPPORTED), top_k >= 1.  scores and idx 4-byte aligned. */
+int fmha_topk_select(const float* scores, int32_t* idx, int rows, int P, int top_k,
+                     void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* fmha_status_string(int status);
 

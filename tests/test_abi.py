@@ -15,7 +15,11 @@ HEADER = os.path.join(ROOT, "include", "fmha_mqa.h")
 def _lib_path():
     path = os.path.join(ROOT, "fmha_mqa_fwd_amd", "libfmha_mqa.so")
     if not os.path.exists(path):  # build only when nothing is built
-        from fmha_mqa_fwd_amd import build as b
+        import importlib.util  # by path: the package import needs the library
+        spec = importlib.util.spec_from_file_location(
+            "fmha_mqa_build", os.path.join(ROOT, "fmha_mqa_fwd_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
     return path
 
@@ -27,9 +31,10 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["fmha_attention_sink", "fmha_lse_merge", "fmha_mqa_fwd",
-                                     "fmha_mqa_fwd_sink", "fmha_mqa_workspace_bytes",
-                                     "fmha_status_string"]
+    assert _declared_functions() == ["fmha_attention_sink", "fmha_index_scores",
+                                     "fmha_lse_merge", "fmha_mqa_fwd", "fmha_mqa_fwd_sink",
+                                     "fmha_mqa_workspace_bytes", "fmha_status_string",
+                                     "fmha_topk_select"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -148,3 +153,32 @@ def test_fwd_sink_requires_a_sink(F):
 ])
 def test_attention_sink_validates(F, args, status):
     assert F._binding._lib.fmha_attention_sink(*args) == status
+
+
+# ------------------------------------------------------------ top-k indexer
+@pytest.mark.parametrize("args,status", [
+    ((A, A, A, A, 1, 2, 48, 128, 100, None), 2),    # index heads not 32/64
+    ((A, A, A, A, 1, 2, 64, 96, 100, None), 2),     # width not 64/128
+    ((A, A, A, A, -1, 2, 64, 128, 100, None), 1),
+    ((A, A, A, A, 1, 2, 64, 128, 0, None), 1),      # empty pool
+    ((None, A, A, A, 1, 2, 64, 128, 100, None), 1),
+    ((A, A, None, A, 1, 2, 64, 128, 100, None), 1),
+    ((A + 8, A, A, A, 1, 2, 64, 128, 100, None), 3),
+    ((A, A, A, A + 2, 1, 2, 64, 128, 100, None), 3),
+    ((None, None, None, None, 0, 5, 64, 128, 100, None), 0),  # no tokens: no-op
+])
+def test_index_scores_validates(F, args, status):
+    assert F._binding._lib.fmha_index_scores(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, A, 4, 0, 8, None), 1),
+    ((A, A, 4, 100, 0, None), 1),
+    ((A, A, -1, 100, 8, None), 1),
+    ((A, A, 4, 40000, 8, None), 2),     # row longer than the LDS selection holds
+    ((None, A, 4, 100, 8, None), 1),
+    ((A, A + 2, 4, 100, 8, None), 3),
+    ((None, None, 0, 100, 8, None), 0),
+])
+def test_topk_select_validates(F, args, status):
+    assert F._binding._lib.fmha_topk_select(*args) == status
