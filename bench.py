@@ -175,6 +175,40 @@ class SourcesCase:
             raise RuntimeError(f"fmha_lse_merge failed: status {st}")
 
 
+class IndexerCase:
+    """The top-k indexer at the sparse top-k config's shape (B=4, T=512, a
+    32768-entry pool, top-k 1024) with 64 index heads of width 128: `part`
+    'scores' times fmha_index_scores, 'select' times fmha_topk_select on the
+    scores it produced."""
+
+    def __init__(self, dev, part, B=4, T=512, H=64, c=128, P=32768, top_k=1024):
+        import fmha_mqa_fwd_amd as F
+
+        g = torch.Generator().manual_seed(4001)
+        self.q = torch.randn(B, T, H, c, generator=g).to(torch.bfloat16).to(dev)
+        self.k = torch.randn(P, c, generator=g).to(torch.bfloat16).to(dev)
+        self.w = (torch.rand(B, T, H, generator=g) * 2 - 1).to(dev)
+        self.scores = torch.empty((B, T, P), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((B, T, top_k), dtype=torch.int32, device=dev)
+        self.F, self.part, self.top_k = F, part, top_k
+        F.index_scores(self.q, self.k, self.w, scores=self.scores)
+        tokens = B * T
+        if part == "scores":
+            self.flops = 2 * tokens * H * c * P
+            self.bytes = tokens * H * c * 2 + P * c * 2 + tokens * H * 4 + tokens * P * 4
+        else:
+            self.flops = 0
+            self.bytes = tokens * P * 4 + tokens * top_k * 4
+        self.desc = (f"top-k indexer {part}: {tokens} tokens, {H} index heads x {c}, "
+                     f"{P}-entry pool, top-k {top_k}")
+
+    def __call__(self):
+        if self.part == "scores":
+            self.F.index_scores(self.q, self.k, self.w, scores=self.scores)
+        else:
+            self.F.topk_select(self.scores, self.top_k, idx=self.idx)
+
+
 def time_case(case, steps, warmup, flush_buf):
     """Mean per-call time in ms: flushed (events around each call, cache
     flushed before it) and warm (events around `steps` back-to-back calls)."""
@@ -490,11 +524,13 @@ def main():
                                                         name="hd512_flash_topk"), dev)),
         ("decode_sink", lambda: Case(3, dev, sink=True)),
         ("two_source_decode", lambda: SourcesCase(dev)),
+        ("indexer_scores", lambda: IndexerCase(dev, "scores")),
+        ("indexer_select", lambda: IndexerCase(dev, "select")),
     )
     for name, make in nxt_cases:
         case = make()
         t = time_case(case, args.steps, args.warmup, flush_buf)
-        if isinstance(case, SourcesCase):
+        if isinstance(case, (SourcesCase, IndexerCase)):
             flops, nbytes, desc = case.flops, case.bytes, case.desc
         else:
             flops, nbytes, desc = case.w.flops, case.w.algorithmic_bytes(), case.w.describe()
