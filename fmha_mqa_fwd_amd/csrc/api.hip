@@ -97,16 +97,20 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* kv_idx,
   const WsLayout wl = ws_layout(rows, hd, num_splits);
   if (!workspace || !aligned(workspace, 16) || workspace_bytes < wl.total)
     return FMHA_ERR_WORKSPACE;
-  float* o_part = static_cast<float*>(workspace);
+  // bf16 outputs keep bf16 partials (their rounding is of the output's own
+  // order; the partial traffic halves); fp32 outputs keep fp32 partials
+  const bool bf16_parts = out_dtype == FMHA_BF16;
+  void* o_part = workspace;
   float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.lse_off);
   p.out = o_part;
   p.lse = lse_part;
-  p.out_mode = fmha::OUT_PARTIAL;
+  p.out_mode = bf16_parts ? fmha::OUT_PARTIAL_BF16 : fmha::OUT_PARTIAL;
   int s = launch_status(fmha::launch_fwd(p, hd, st));
   if (s != FMHA_OK) return s;
   // the sink joins once, in the merge (the partials carry none)
   return launch_status(fmha::launch_merge(o_part, lse_part, num_splits, (int)rows, hd, out,
-                                          out_dtype == FMHA_BF16, lse, st, sink, n_h));
+                                          out_dtype == FMHA_BF16, lse, st, sink, n_h,
+                                          bf16_parts));
 }
 
 }  // namespace

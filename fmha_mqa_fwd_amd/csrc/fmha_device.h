@@ -281,7 +281,7 @@ struct Rows {
   }
 
   // O / l and lse = (m + log2 l) ln 2; an empty row (no key seen) gets O = 0,
-  // lse = -inf.  OUT_PARTIAL writes fp32 to plane `split` of [splits, rows, HD].
+  // lse = -inf.  Partial modes write plane `split` of [splits, rows, HD].
   // Direct form: each lane stores its own 4-element pieces (a row's 32-wide d
   // block arrives as 8 pieces from 2 lanes per instruction).
   // col0: first output column this wave holds; write_lse: this wave writes
@@ -298,9 +298,9 @@ struct Rows {
       const int r = row0 + qb * 32 + l32;
       if (r >= p.rows_per_group) continue;
       const int64_t row = grow0 + r;
-      if (p.sink != nullptr && p.out_mode != OUT_PARTIAL)
+      if (p.sink != nullptr && !is_partial(p.out_mode))
         sink_adjust(p.sink[row % p.n_heads], inv, lse_v);
-      const int64_t base = (p.out_mode == OUT_PARTIAL) ? (int64_t)split * p.total_rows : 0;
+      const int64_t base = is_partial(p.out_mode) ? (int64_t)split * p.total_rows : 0;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -309,9 +309,10 @@ struct Rows {
           f32x4 val;
 #pragma unroll
           for (int i = 0; i < 4; ++i) val[i] = o[db][qb][4 * rg + i] * inv;
-          if (p.out_mode == OUT_BF16) {
+          if (is_bf16(p.out_mode)) {
             u32x2 w = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row * LD + col0 + d) = w;
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (base + row) * LD + col0 +
+                                      d) = w;
           } else {
             *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + (base + row) * LD + col0 + d) =
                 val;
@@ -333,13 +334,13 @@ struct Rows {
                                             bool write_lse = true) const {
     const int l32 = lane & 31;
     const int hlf = lane >> 5;
-    const bool bf = (p.out_mode == OUT_BF16);
+    const bool bf = is_bf16(p.out_mode);
     const int esz = bf ? 2 : 4;
     const int rb = HD * esz;            // bytes of a row this wave holds
     const int64_t grb = (int64_t)LD * esz;  // bytes of a whole output row
     const int cpr = rb / 16;            // 16-byte chunks per row (8 .. 64)
     const int swm = cpr >= 16 ? 15 : 7;
-    const int64_t base = (p.out_mode == OUT_PARTIAL) ? (int64_t)split * p.total_rows : 0;
+    const int64_t base = is_partial(p.out_mode) ? (int64_t)split * p.total_rows : 0;
     char* const out = static_cast<char*>(p.out);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -347,7 +348,7 @@ struct Rows {
       const bool empty = (m[qb] == neg_inf());
       float inv = empty ? 0.f : 1.f / lt;
       float lse_v = empty ? neg_inf() : (m[qb] + log2f(lt)) * LN2;
-      if (p.sink != nullptr && p.out_mode != OUT_PARTIAL) {
+      if (p.sink != nullptr && !is_partial(p.out_mode)) {
         const int rs = row0 + qb * 32 + l32;
         if (rs < p.rows_per_group) sink_adjust(p.sink[(grow0 + rs) % p.n_heads], inv, lse_v);
       }

@@ -308,7 +308,7 @@ void fwd_kernel(FwdParams p) {
   constexpr int STAGE_BYTES = NKI * 1024;
   static_assert(QW == 32, "epilogue staging assumes 32 rows per wave");
   if constexpr (WAVES == 4 && 2 * QW * RB_BF16 <= STAGE_BYTES) {
-    if (p.out_mode == OUT_BF16) {
+    if (is_bf16(p.out_mode)) {
       char* const region = (wave < 2 ? sK0 : sK1) + (wave & 1) * QW * RB_BF16;
       w.store_lds(p, grow0, row0, split, lane, [&](int r) { return region + r * RB_BF16; }, col0,
                   dh == 0);

@@ -7,7 +7,16 @@
 
 namespace fmha {
 
-enum OutMode : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_PARTIAL = 2 };
+// OUT_PARTIAL(_BF16): split partials, normalised O as fp32 (bf16) in plane
+// `split` of [num_splits, total_rows, hd], lse fp32 [num_splits, total_rows].
+enum OutMode : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_PARTIAL = 2, OUT_PARTIAL_BF16 = 3 };
+
+__host__ __device__ inline bool is_partial(int mode) {
+  return mode == OUT_PARTIAL || mode == OUT_PARTIAL_BF16;
+}
+__host__ __device__ inline bool is_bf16(int mode) {
+  return mode == OUT_BF16 || mode == OUT_PARTIAL_BF16;
+}
 
 // One launch of the attention kernel.  Rows r = (b*T + t)*n_h + h of q/out are
 // split into groups that share one K/V set: a batch (dense, T*n_h rows) or a
@@ -18,7 +27,7 @@ struct FwdParams {
   const uint16_t* v;        // same layout as k
   const int32_t* kv_idx;    // gather: int32 [n_groups, s_k]; dense: nullptr
   void* out;                // OUT_F32/OUT_BF16: [total_rows, hd];
-                            // OUT_PARTIAL: fp32 [num_splits, total_rows, hd]
+                            // partial modes: [num_splits, total_rows, hd]
   float* lse;               // [total_rows] or, partial, [num_splits, total_rows]
   int64_t total_rows;
   int rows_per_group;
@@ -48,11 +57,13 @@ int chunk_max_keys(int hd);
 hipError_t launch_chunk(FwdParams p, int hd, hipStream_t stream);
 
 // out[r] = sum_i w_i o_i[r] / sum_i w_i with w_i = exp(lse_i[r] - max_i lse_i[r]).
-// With sink (optional, [n_heads]), the sink of row r's head r % n_heads joins
-// the merged result (see sink_adjust in fmha_device.h).
-hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_parts,
+// o_parts holds fp32, or bf16 when parts_bf16.  With sink (optional,
+// [n_heads]), the sink of row r's head r % n_heads joins the merged result
+// (see sink_adjust in fmha_device.h).
+hipError_t launch_merge(const void* o_parts, const float* lse_parts, int n_parts,
                         int rows, int hd, void* out, bool out_bf16, float* lse,
-                        hipStream_t stream, const float* sink = nullptr, int n_heads = 1);
+                        hipStream_t stream, const float* sink = nullptr, int n_heads = 1,
+                        bool parts_bf16 = false);
 
 // In place: out[r] *= exp(lse[r] - lse'[r]), lse'[r] = ln(exp(lse[r]) + exp(sink[r % n_heads])).
 hipError_t launch_sink(void* out, float* lse, const float* sink, int rows, int n_heads, int hd,

@@ -28,8 +28,10 @@ constexpr float LN2 = 0.6931471805599453f;
 // NP > 0: the part count is a compile-time constant, so every lse and O load
 // of a thread is issued before any arithmetic (one memory round trip per
 // thread instead of one per part).  NP == 0: any count, loop over parts.
-template <bool OUT_BF16, int NP>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_parts,
+// IN_BF16: the parts hold bf16 (the split path's own partials for bf16
+// outputs), else fp32.
+template <bool OUT_BF16, int NP, bool IN_BF16>
+__global__ __launch_bounds__(256) void merge_kernel(const void* __restrict__ o_parts,
                                                     const float* __restrict__ lse_parts,
                                                     int n_parts, int rows, int hd,
                                                     void* __restrict__ out,
@@ -43,6 +45,16 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += stride) {
     const int row = (int)(u / cpr);
     const int ch = (int)(u % cpr);
+    auto part = [&](int i) __attribute__((always_inline)) -> f32x4 {
+      const int64_t off = ((int64_t)i * rows + row) * hd + 4 * ch;
+      if constexpr (IN_BF16) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(o_parts) + off);
+        return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                     __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+      } else {
+        return *reinterpret_cast<const f32x4*>(static_cast<const float*>(o_parts) + off);
+      }
+    };
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float mx = -__builtin_inff();
     float den = 0.f;
@@ -52,8 +64,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
 #pragma unroll
       for (int i = 0; i < NP; ++i) li[i] = lse_parts[(int64_t)i * rows + row];
 #pragma unroll
-      for (int i = 0; i < NP; ++i)
-        oi[i] = *reinterpret_cast<const f32x4*>(o_parts + ((int64_t)i * rows + row) * hd + 4 * ch);
+      for (int i = 0; i < NP; ++i) oi[i] = part(i);
 #pragma unroll
       for (int i = 0; i < NP; ++i) mx = fmaxf(mx, li[i]);
       if (mx != -__builtin_inff()) {
@@ -75,8 +86,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
           if (li == -__builtin_inff()) continue;  // empty part: its o_i is never read
           const float w = __builtin_amdgcn_exp2f((li - mx) * LOG2E);
           den += w;
-          const f32x4 oi =
-              *reinterpret_cast<const f32x4*>(o_parts + ((int64_t)i * rows + row) * hd + 4 * ch);
+          const f32x4 oi = part(i);
           acc += w * oi;
         }
         acc *= 1.f / den;
@@ -131,22 +141,26 @@ __global__ __launch_bounds__(256) void sink_kernel(void* __restrict__ out, float
 }
 
 template <int NP>
-void launch_np(bool out_bf16, dim3 grid, hipStream_t stream, const float* o_parts,
-               const float* lse_parts, int n_parts, int rows, int hd, void* out, float* lse,
-               const float* sink, int n_heads) {
-  if (out_bf16)
-    hipLaunchKernelGGL((merge_kernel<true, NP>), grid, dim3(256), 0, stream, o_parts, lse_parts,
-                       n_parts, rows, hd, out, lse, sink, n_heads);
+void launch_np(bool out_bf16, bool parts_bf16, dim3 grid, hipStream_t stream,
+               const void* o_parts, const float* lse_parts, int n_parts, int rows, int hd,
+               void* out, float* lse, const float* sink, int n_heads) {
+  // bf16 parts come only with bf16 outputs
+  if (parts_bf16)
+    hipLaunchKernelGGL((merge_kernel<true, NP, true>), grid, dim3(256), 0, stream, o_parts,
+                       lse_parts, n_parts, rows, hd, out, lse, sink, n_heads);
+  else if (out_bf16)
+    hipLaunchKernelGGL((merge_kernel<true, NP, false>), grid, dim3(256), 0, stream, o_parts,
+                       lse_parts, n_parts, rows, hd, out, lse, sink, n_heads);
   else
-    hipLaunchKernelGGL((merge_kernel<false, NP>), grid, dim3(256), 0, stream, o_parts, lse_parts,
-                       n_parts, rows, hd, out, lse, sink, n_heads);
+    hipLaunchKernelGGL((merge_kernel<false, NP, false>), grid, dim3(256), 0, stream, o_parts,
+                       lse_parts, n_parts, rows, hd, out, lse, sink, n_heads);
 }
 
 }  // namespace
 
-hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_parts, int rows,
+hipError_t launch_merge(const void* o_parts, const float* lse_parts, int n_parts, int rows,
                         int hd, void* out, bool out_bf16, float* lse, hipStream_t stream,
-                        const float* sink, int n_heads) {
+                        const float* sink, int n_heads, bool parts_bf16) {
   const int64_t total = (int64_t)rows * (hd / 4);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
@@ -155,16 +169,16 @@ hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_part
   switch (n_parts) {
 #define FMHA_MERGE_CASE(N) \
   case N:                  \
-    launch_np<N>(out_bf16, grid, stream, o_parts, lse_parts, n_parts, rows, hd, out, lse, sink, \
-                 n_heads);                                                                     \
+    launch_np<N>(out_bf16, parts_bf16, grid, stream, o_parts, lse_parts, n_parts, rows, hd, out, \
+                 lse, sink, n_heads);                                                              \
     break;
     FMHA_MERGE_CASE(1) FMHA_MERGE_CASE(2) FMHA_MERGE_CASE(3) FMHA_MERGE_CASE(4)
     FMHA_MERGE_CASE(5) FMHA_MERGE_CASE(6) FMHA_MERGE_CASE(7) FMHA_MERGE_CASE(8)
     FMHA_MERGE_CASE(12) FMHA_MERGE_CASE(16)
 #undef FMHA_MERGE_CASE
     default:
-      launch_np<0>(out_bf16, grid, stream, o_parts, lse_parts, n_parts, rows, hd, out, lse, sink,
-                   n_heads);
+      launch_np<0>(out_bf16, parts_bf16, grid, stream, o_parts, lse_parts, n_parts, rows, hd, out,
+                   lse, sink, n_heads);
   }
   return hipGetLastError();
 }
