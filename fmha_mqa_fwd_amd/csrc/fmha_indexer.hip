@@ -17,11 +17,12 @@
 // lane holds one entry and 16 of the 32 heads, so the weighted ReLU sum over
 // heads is in-lane plus one v_permlane32_swap.
 //
-// topk_kernel: one workgroup per token; the row's scores, mapped to
-// order-preserving 32-bit keys, sit in LDS; a 4-pass radix select (8 bits per
-// pass, LDS histograms) finds the top_k-th key exactly, then a pass in entry
-// order writes every entry above it and the first entries equal to it, with
-// wave ballots for the prefix counts.
+// topk_kernel: one 1024-thread workgroup per token; the row's scores, mapped to
+// order-preserving 32-bit keys, stay in VGPRs (32 per thread).  A 3-pass radix
+// select (12, 12, 8 bits; LDS histograms, only the first pass counting every
+// key) finds the top_k-th key exactly, then a pass in entry order writes every
+// entry above it and the first entries equal to it, ranked by wave ballots and
+// one scan of per-(chunk, wave) counts.
 #include "fmha_device.h"
 
 namespace fmha {
@@ -147,132 +148,254 @@ void score_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 }
 
 // ------------------------------------------------------------- selection
-constexpr int SEL_THREADS = 256;
-constexpr int SEL_MAX_P = 32768;  // a row's keys fit in LDS (128 KiB)
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int SEL_MAX_P = 32768;                 // a row's keys fit in VGPRs
+constexpr int SEL_J = SEL_MAX_P / SEL_THREADS;   // keys per thread
+constexpr int SEL_BINS = 4096;                   // 12-bit digits (the last pass: 8)
+constexpr int SEL_CAND = 2048;  // boundary-digit keys kept in LDS for passes 2 and 3
 
-// Order-preserving map of a float to uint32 (-0 taken as +0).
+// Order-preserving map of a float score to a 32-bit key (-0 and +0 equal).
 __device__ __forceinline__ uint32_t order_key(float f) {
   f += 0.f;
   const uint32_t b = __float_as_uint(f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Exclusive prefix count of `flag` over the workgroup's threads in thread
-// order, and the workgroup total (every thread calls it; uses wsum[4]).
-__device__ __forceinline__ int block_prefix(bool flag, int* wsum, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t m = __ballot(flag);
-  const int in_wave = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-  if (lane == 0) wsum[wave] = __popcll(m);
-  __syncthreads();
-  int before = 0;
-  total = 0;
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts within
+// each 16-lane row, then row broadcasts of lane 15 and lane 31 (GFX9 DPP).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false); // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false); // row_bcast:31 -> rows 2, 3
+  return (uint32_t)x;
+}
+
+// Sums of wtot[0 .. nw) over the waves before this one and over all of them,
+// by one more wave scan (lane l holds wtot[l]) and two readlanes.
+__device__ __forceinline__ void wave_totals(const uint32_t* wtot, int nw, uint32_t& before,
+                                            uint32_t& total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t incl = wave_incl_scan(lane < nw ? wtot[lane] : 0u);
+  total = (uint32_t)__builtin_amdgcn_readlane((int)incl, nw - 1);
+  before = wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)incl, wave - 1) : 0u;
+}
+
+// One radix step: `hist` holds the digit counts of the keys that share the
+// prefix found so far; find the digit of the krem-th largest of them (the
+// highest digit b with count(> b) < krem <= count(>= b)) and record the new
+// prefix, the rank left in it and the digit's count in s[0], s[1], s[2].  NB digits, NB / SEL_THREADS per thread
+// (or one digit for the first NB threads).  Starts and ends with a barrier's
+// worth of ordering: every thread must call it.
+template <int NB>
+__device__ __forceinline__ void radix_step(const int* hist, uint32_t* wtot, uint32_t* s,
+                                           uint32_t prefix, int shift, int krem) {
+  constexpr int BPT = NB >= SEL_THREADS ? NB / SEL_THREADS : 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool owner = tid * BPT < NB;
+  int c[BPT];
+  uint32_t mine = 0;
 #pragma unroll
-  for (int w = 0; w < SEL_THREADS / 64; ++w) {
-    const int c = wsum[w];
-    before += w < wave ? c : 0;
-    total += c;
+  for (int b = 0; b < BPT; ++b) {
+    c[b] = owner ? hist[tid * BPT + b] : 0;
+    mine += c[b];
   }
-  __syncthreads();  // wsum reused by the next call
-  return before + in_wave;
+  const uint32_t incl = wave_incl_scan(mine);
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  uint32_t before, total;
+  wave_totals(wtot, SEL_WAVES, before, total);
+  // keys in digits above this thread's: everything after it in digit order
+  int cum = (int)(total - (before + incl));
+#pragma unroll
+  for (int b = BPT - 1; b >= 0; --b) {
+    if (owner && cum < krem && cum + c[b] >= krem) {
+      s[0] = prefix | ((uint32_t)(tid * BPT + b) << shift);
+      s[1] = (uint32_t)(krem - cum);
+      s[2] = (uint32_t)c[b];
+    }
+    cum += c[b];
+  }
+  __syncthreads();
+}
+
+// Keeps the compiler from reusing one loop's comparisons in a later loop
+// (64 ballot masks would spill); recomputing them costs one VALU each.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(const float* __restrict__ scores,
                                                            int32_t* __restrict__ idx, int P,
                                                            int top_k) {
-  __shared__ uint32_t sKey[SEL_MAX_P];
-  __shared__ int hist[256];
-  __shared__ int wsum[SEL_THREADS / 64];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_krem;
+  __shared__ int histA[SEL_BINS];
+  __shared__ int histB[SEL_BINS];
+  __shared__ uint32_t cand[SEL_CAND];
+  __shared__ uint32_t cnt[SEL_J * SEL_WAVES];  // per (chunk, wave) counts, then their prefix
+  __shared__ uint32_t wtot[SEL_WAVES];
+  __shared__ uint32_t s_sel[3];                // prefix, rank left in it, its digit's count
+  __shared__ int s_ncand;
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const float* src = scores + row * P;
   int32_t* dst = idx + row * top_k;
   const int n = min(top_k, P);
-  if (n <= 0) {
-    for (int i = tid; i < top_k; i += SEL_THREADS) dst[i] = -1;
-    return;
-  }
-
-  for (int i = tid; i < P; i += SEL_THREADS) sKey[i] = order_key(src[i]);
-  if (tid == 0) {
-    s_prefix = 0;
-    s_krem = n;
-  }
-  __syncthreads();
-
-  // radix select of the n-th largest key, most significant byte first
-  uint32_t mask = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0;
-    __syncthreads();
-    const uint32_t prefix = s_prefix;
-    for (int i = tid; i < P; i += SEL_THREADS) {
-      const uint32_t u = sKey[i];
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane l owns bins 4l .. 4l+3; suffix sums from the top bin down
-      const int lane = tid;
-      const int c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
-                c3 = hist[4 * lane + 3];
-      const int mine = c0 + c1 + c2 + c3;
-      int suf = mine;  // inclusive suffix sum over lanes lane .. 63
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_down(suf, d);
-        if (lane + d < 64) suf += o;
-      }
-      const int above = suf - mine;  // keys in bins owned by higher lanes
-      const int krem = s_krem;
-      // the bin holding the krem-th largest: the highest bin b with
-      // count(bins > b) < krem <= count(bins >= b)
-      int found = -1, newk = 0;
-      int cum = above;
-      const int c[4] = {c0, c1, c2, c3};
-#pragma unroll
-      for (int b = 3; b >= 0; --b) {
-        if (found < 0 && cum < krem && cum + c[b] >= krem) {
-          found = 4 * lane + b;
-          newk = krem - cum;
-        }
-        cum += c[b];
-      }
-      const uint64_t who = __ballot(found >= 0);
-      const int src_lane = 63 - __builtin_clzll(who);
-      const int bin = __shfl(found, src_lane);
-      const int k2 = __shfl(newk, src_lane);
-      if (lane == 0) {
-        s_prefix = prefix | ((uint32_t)bin << shift);
-        s_krem = k2;
-      }
-    }
-    __syncthreads();
-    mask |= 255u << shift;
-  }
-  const uint32_t T = s_prefix;   // the n-th largest key
-  const int take_eq = s_krem;    // how many keys equal to T are kept
-  __syncthreads();
-
-  // entries above T, and the first take_eq entries equal to T, in entry order
-  int eq_run = 0, sel_run = 0;
-  for (int base = 0; base < P; base += SEL_THREADS) {
-    const int i = base + tid;
-    const uint32_t u = i < P ? sKey[i] : 0u;
-    const bool gt = i < P && u > T;
-    const bool eq = i < P && u == T;
-    int eq_tot, sel_tot;
-    const int eq_before = eq_run + block_prefix(eq, wsum, eq_tot);
-    const bool sel = gt || (eq && eq_before < take_eq);
-    const int pos = sel_run + block_prefix(sel, wsum, sel_tot);
-    if (sel) dst[pos] = i;
-    eq_run += eq_tot;
-    sel_run += sel_tot;
-  }
   for (int i = n + tid; i < top_k; i += SEL_THREADS) dst[i] = -1;
+  if (n <= 0) return;
+
+  // key j of this thread is entry j * SEL_THREADS + tid (coalesced loads).
+  // Buffer loads (past the row's end they read zero) with one shared 32-bit
+  // offset: no predication and no per-load address, so all SEL_J loads are in
+  // flight together.
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, P * 4, BUF_FLAGS);
+  uint32_t u[SEL_J];
+#pragma unroll
+  for (int j = 0; j < SEL_J; ++j)
+    u[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, j * SEL_THREADS * 4, 0);
+  // Entries past the row's end get key 0, the smallest key.  Rather than test
+  // validity per key in every pass, their count (pad) is taken back out of
+  // digit 0 in each pass whose prefix they share; in entry order they come
+  // after every real entry, so the compaction never selects them.
+  const int jn = (P - tid + SEL_THREADS - 1) / SEL_THREADS;  // this thread's real keys
+  const int jfull = P / SEL_THREADS;                         // chunks real for every thread
+#pragma unroll
+  for (int j = 0; j < SEL_J; ++j) u[j] = order_key(__uint_as_float(u[j]));
+  if (jfull < SEL_J) {
+#pragma unroll
+    for (int j = 0; j < SEL_J; ++j)
+      if (j >= jfull) u[j] = j < jn ? u[j] : 0u;
+  }
+  const int pad = SEL_MAX_P - P;
+#pragma unroll
+  for (int b = 0; b < SEL_BINS / SEL_THREADS; ++b) {
+    histA[b * SEL_THREADS + tid] = 0;
+    histB[b * SEL_THREADS + tid] = 0;
+  }
+  if (tid == 0) s_ncand = 0;
+  __syncthreads();
+
+  // pass 1: bits 31..20 of every key
+  if (tid == 0) atomicAdd(&histA[0], -pad);
+#pragma unroll
+  for (int j = 0; j < SEL_J; ++j) atomicAdd(&histA[u[j] >> 20], 1);
+  __syncthreads();
+  radix_step<SEL_BINS>(histA, wtot, s_sel, 0u, 20, n);
+  uint32_t prefix = s_sel[0];
+  int krem = (int)s_sel[1];
+  const int c1 = (int)s_sel[2];  // keys in the boundary digit
+  if (tid < 256) histA[tid] = 0;  // pass 1's counts were all read before the step's last barrier
+
+  // Passes 2 and 3 only look at the boundary digit's keys: gathered into LDS
+  // when few (and not sharing digit 0 with the padding), else re-scanned in
+  // VGPRs.
+  const bool use_cand = c1 <= SEL_CAND && (prefix >> 20) != 0;
+  if (use_cand) {
+#pragma unroll
+    for (int j = 0; j < SEL_J; ++j)
+      if ((u[j] ^ prefix) < (1u << 20)) cand[atomicAdd(&s_ncand, 1)] = u[j];
+    __syncthreads();
+    for (int k = tid; k < c1; k += SEL_THREADS)
+      atomicAdd(&histB[(cand[k] >> 8) & (SEL_BINS - 1)], 1);
+  } else {
+    if (tid == 0 && (prefix >> 20) == 0) atomicAdd(&histB[0], -pad);
+#pragma unroll
+    for (int j = 0; j < SEL_J; ++j)
+      if ((u[j] ^ prefix) < (1u << 20)) atomicAdd(&histB[(u[j] >> 8) & (SEL_BINS - 1)], 1);
+  }
+  __syncthreads();
+  radix_step<SEL_BINS>(histB, wtot, s_sel, prefix, 8, krem);
+  prefix = s_sel[0];
+  krem = (int)s_sel[1];
+
+  // pass 3: bits 7..0
+  if (use_cand) {
+    for (int k = tid; k < c1; k += SEL_THREADS) {
+      const uint32_t v = cand[k];
+      if ((v ^ prefix) < 256u) atomicAdd(&histA[v & 255], 1);
+    }
+  } else {
+    if (tid == 0 && (prefix >> 8) == 0) atomicAdd(&histA[0], -pad);
+#pragma unroll
+    for (int j = 0; j < SEL_J; ++j)
+      if ((u[j] ^ prefix) < 256u) atomicAdd(&histA[u[j] & 255], 1);
+  }
+  __syncthreads();
+  radix_step<256>(histA, wtot, s_sel, prefix, 0, krem);
+  const uint32_t T = s_sel[0];        // the n-th largest key
+  const int take_eq = (int)s_sel[1];  // how many keys equal to T are kept (the first ones)
+  const int n_eq = (int)s_sel[2];     // how many keys equal T
+
+  // Ordered compaction: entries above T and the first take_eq entries equal
+  // to T, in entry order.  Per (chunk, wave) counts, one exclusive scan of
+  // them in entry order, then in-wave ranks from the ballots.  Usually every
+  // key equal to T is kept (T > 0 then also excludes the padding): one mask,
+  // u >= T.  Otherwise the ranks of the keys above T and equal to T are kept
+  // apart (packed gt | eq << 16; each count fits 16 bits, so the packed sums
+  // do not carry).
+  const bool all_eq = take_eq == n_eq && T != 0u;
+  const __amdgpu_buffer_rsrc_t rd =
+      __builtin_amdgcn_make_buffer_rsrc((void*)dst, (short)0, n * 4, BUF_FLAGS);
+  uint32_t my_cnt = 0;  // lane j: this wave's count in chunk j
+#pragma unroll
+  for (int j = 0; j < SEL_J; ++j) {
+    uint32_t c;
+    if (all_eq) {
+      c = (uint32_t)__popcll(__ballot(u[j] >= T));
+    } else {
+      c = (uint32_t)__popcll(__ballot(u[j] > T)) |
+          ((uint32_t)__popcll(__ballot(u[j] == T)) << 16);
+    }
+    asm("v_writelane_b32 %0, %1, m0" : "+v"(my_cnt) : "s"(c), "{m0}"(j));
+  }
+  if (lane < SEL_J) cnt[lane * SEL_WAVES + wave] = my_cnt;
+  __syncthreads();
+  constexpr int NC = SEL_J * SEL_WAVES;
+  static_assert(NC <= SEL_THREADS && SEL_J <= 64, "one count per thread");
+  uint32_t v = 0, incl = 0;
+  if (tid < NC) {
+    v = cnt[tid];
+    incl = wave_incl_scan(v);
+    if (lane == 63) wtot[wave] = incl;
+  }
+  __syncthreads();
+  if (tid < NC) {
+    uint32_t before, total;
+    wave_totals(wtot, NC / 64, before, total);
+    cnt[tid] = before + incl - v;  // exclusive prefix; each thread rewrites only its own entry
+  }
+  __syncthreads();
+  const uint32_t basev = lane < SEL_J ? cnt[lane * SEL_WAVES + wave] : 0u;  // lane j: chunk j's base
+  const uint32_t T2 = opaque(T);
+#pragma unroll
+  for (int j = 0; j < SEL_J; ++j) {
+    const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)basev, j);
+    const uint32_t id = (uint32_t)(j * SEL_THREADS + tid);
+    if (all_eq) {
+      const bool hit = u[j] >= T2;
+      const uint64_t m = __ballot(hit);
+      const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, base));
+      if (hit) __builtin_amdgcn_raw_buffer_store_b32(id, rd, (int)(pos * 4), 0, 0);
+    } else {
+      const bool gt = u[j] > T2, eq = u[j] == T2;
+      const uint64_t mg = __ballot(gt), me = __ballot(eq);
+      const int gt_before = (int)__builtin_amdgcn_mbcnt_hi(
+          (uint32_t)(mg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mg, base & 0xffffu));
+      const int eq_before = (int)__builtin_amdgcn_mbcnt_hi(
+          (uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, base >> 16));
+      if (gt || (eq && eq_before < take_eq))
+        __builtin_amdgcn_raw_buffer_store_b32(id, rd, (gt_before + min(eq_before, take_eq)) * 4,
+                                              0, 0);
+    }
+  }
 }
 
 template <int C, int H>
