@@ -7,7 +7,7 @@
 // exponential overflows; the merged lse is max + ln(sum of shifted weights).
 //
 // The kernel is bound by HBM/L2 bandwidth: each thread owns one 16-byte chunk
-// (4 floats) of one output row, reads that chunk from every part with 16-byte
+// of every part's row (4 fp32 or 8 bf16 elements), reads it with 16-byte
 // loads (consecutive threads -> consecutive chunks of a row, so every wave
 // reads whole contiguous segments) and writes it once.  For the usual part
 // counts all of a thread's loads are in flight together.
@@ -20,6 +20,7 @@ namespace {
 
 using dev::f32x4;
 using dev::u32x2;
+using dev::u32x4;
 using dev::pack_bf16x2;
 
 constexpr float LOG2E = 1.4426950408889634f;
@@ -29,7 +30,8 @@ constexpr float LN2 = 0.6931471805599453f;
 // of a thread is issued before any arithmetic (one memory round trip per
 // thread instead of one per part).  NP == 0: any count, loop over parts.
 // IN_BF16: the parts hold bf16 (the split path's own partials for bf16
-// outputs), else fp32.
+// outputs, whose output rows are 16-byte aligned), else fp32.  A thread owns
+// one 16-byte chunk of every part's row: 8 elements of bf16 parts, 4 of fp32.
 template <bool OUT_BF16, int NP, bool IN_BF16>
 __global__ __launch_bounds__(256) void merge_kernel(const void* __restrict__ o_parts,
                                                     const float* __restrict__ lse_parts,
@@ -38,33 +40,42 @@ __global__ __launch_bounds__(256) void merge_kernel(const void* __restrict__ o_p
                                                     float* __restrict__ lse,
                                                     const float* __restrict__ sink,
                                                     int n_heads) {
-  const int cpr = hd >> 2;  // 16-byte chunks per row
+  constexpr int E = IN_BF16 ? 8 : 4;  // elements per thread
+  static_assert(!IN_BF16 || OUT_BF16, "bf16 parts come with bf16 outputs");
+  const int cpr = hd / E;  // chunks per row
   const int64_t total = (int64_t)rows * cpr;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int np = NP > 0 ? NP : n_parts;
   for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += stride) {
     const int row = (int)(u / cpr);
     const int ch = (int)(u % cpr);
-    auto part = [&](int i) __attribute__((always_inline)) -> f32x4 {
-      const int64_t off = ((int64_t)i * rows + row) * hd + 4 * ch;
+    auto part = [&](int i, float (&o)[E]) __attribute__((always_inline)) {
+      const int64_t off = ((int64_t)i * rows + row) * hd + E * ch;
       if constexpr (IN_BF16) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(o_parts) + off);
-        return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
-                     __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(o_parts) + off);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          o[2 * k] = __uint_as_float(w[k] << 16);
+          o[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
       } else {
-        return *reinterpret_cast<const f32x4*>(static_cast<const float*>(o_parts) + off);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o_parts) + off);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = v[k];
       }
     };
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float acc[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) acc[k] = 0.f;
     float mx = -__builtin_inff();
     float den = 0.f;
     if constexpr (NP > 0) {
       float li[NP];
-      f32x4 oi[NP];
+      float oi[NP][E];
 #pragma unroll
       for (int i = 0; i < NP; ++i) li[i] = lse_parts[(int64_t)i * rows + row];
 #pragma unroll
-      for (int i = 0; i < NP; ++i) oi[i] = part(i);
+      for (int i = 0; i < NP; ++i) part(i, oi[i]);
 #pragma unroll
       for (int i = 0; i < NP; ++i) mx = fmaxf(mx, li[i]);
       if (mx != -__builtin_inff()) {
@@ -74,9 +85,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const void* __restrict__ o_p
           const bool live = li[i] != -__builtin_inff();
           const float w = live ? __builtin_amdgcn_exp2f((li[i] - mx) * LOG2E) : 0.f;
           den += w;
-          if (live) acc += w * oi[i];
+          if (live) {
+#pragma unroll
+            for (int k = 0; k < E; ++k) acc[k] += w * oi[i][k];
+          }
         }
-        acc *= 1.f / den;
       }
     } else {
       for (int i = 0; i < np; ++i) mx = fmaxf(mx, lse_parts[(int64_t)i * rows + row]);
@@ -86,23 +99,28 @@ __global__ __launch_bounds__(256) void merge_kernel(const void* __restrict__ o_p
           if (li == -__builtin_inff()) continue;  // empty part: its o_i is never read
           const float w = __builtin_amdgcn_exp2f((li - mx) * LOG2E);
           den += w;
-          const f32x4 oi = part(i);
-          acc += w * oi;
+          float oi[E];
+          part(i, oi);
+#pragma unroll
+          for (int k = 0; k < E; ++k) acc[k] += w * oi[k];
         }
-        acc *= 1.f / den;
       }
     }
+    float f = mx != -__builtin_inff() ? 1.f / den : 0.f;
     float lse_r = (mx != -__builtin_inff()) ? mx + log2f(den) * LN2 : -__builtin_inff();
-    if (sink != nullptr) {
-      float f = 1.f;
-      dev::sink_adjust(sink[row % n_heads], f, lse_r);
-      acc *= f;
-    }
+    if (sink != nullptr) dev::sink_adjust(sink[row % n_heads], f, lse_r);
     if constexpr (OUT_BF16) {
-      u32x2 w = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (int64_t)row * hd + 4 * ch) = w;
+      uint32_t w[E / 2];
+#pragma unroll
+      for (int k = 0; k < E / 2; ++k) w[k] = pack_bf16x2(acc[2 * k] * f, acc[2 * k + 1] * f);
+      uint16_t* o = static_cast<uint16_t*>(out) + (int64_t)row * hd + E * ch;
+      if constexpr (E == 8)
+        *reinterpret_cast<u32x4*>(o) = u32x4{w[0], w[1], w[2], w[3]};
+      else
+        *reinterpret_cast<u32x2*>(o) = u32x2{w[0], w[1]};
     } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)row * hd + 4 * ch) = acc;
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)row * hd + E * ch) =
+          f32x4{acc[0] * f, acc[1] * f, acc[2] * f, acc[3] * f};
     }
     if (ch == 0 && lse != nullptr) lse[row] = lse_r;
   }
@@ -161,7 +179,7 @@ void launch_np(bool out_bf16, bool parts_bf16, dim3 grid, hipStream_t stream,
 hipError_t launch_merge(const void* o_parts, const float* lse_parts, int n_parts, int rows,
                         int hd, void* out, bool out_bf16, float* lse, hipStream_t stream,
                         const float* sink, int n_heads, bool parts_bf16) {
-  const int64_t total = (int64_t)rows * (hd / 4);
+  const int64_t total = (int64_t)rows * (hd / (parts_bf16 ? 8 : 4));
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
