@@ -54,7 +54,9 @@ def _select_case(F, scores, top_k):
 
 
 @pytest.mark.parametrize("rows,P,top_k", [(3, 5000, 1024), (2, 32768, 1024), (4, 700, 64),
-                                          (2, 1, 1), (3, 10, 16), (2, 1000, 1000)])
+                                          (2, 1, 1), (3, 10, 16), (2, 1000, 1000),
+                                          (1, 32768, 32768), (2, 32768, 1), (2, 31001, 1024),
+                                          (3, 2047, 2048)])
 def test_selection_is_exact_on_random_scores(F, rows, P, top_k):
     g = torch.Generator().manual_seed(rows * P + top_k)
     _select_case(F, torch.randn(rows, P, generator=g), top_k)
@@ -108,3 +110,25 @@ def test_selected_lists_feed_the_sparse_attention(F):
     m = oracle.row_metrics(out.cpu().numpy().reshape(-1, hd), O.reshape(-1, hd),
                            lse.cpu().numpy().reshape(-1), L.reshape(-1))
     assert m["max_abs"] <= 1e-2 and m["min_row_cos"] >= 0.9999 and m["lse_err"] <= 1e-3, m
+
+
+def test_indexer_at_the_benchmarked_size_sampled(F):
+    """The shape bench.py times (B=4, T=512, 64 index heads x 128, a
+    32768-entry pool, top-k 1024): sampled tokens' scores against float64,
+    and their selections bit-exact against the exact top-k of the GPU's own
+    fp32 scores."""
+    B, T, H, c, P, top_k = 4, 512, 64, 128, 32768, 1024
+    q, k, w = _inputs(B, T, H, c, P, seed=4001)
+    qd, kd, wd = q.to(DEV), k.to(DEV), w.to(DEV)
+    s = F.index_scores(qd, kd, wd)
+    idx = F.topk_select(s, top_k)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    toks = [(int(b), int(t)) for b, t in zip(rng.integers(0, B, 6), rng.integers(0, T, 6))]
+    toks += [(0, 0), (B - 1, T - 1)]
+    for b, t in toks:
+        ref = OI.index_scores(q[b:b + 1, t:t + 1], k, w[b:b + 1, t:t + 1])[0, 0]
+        got = s[b, t].cpu().numpy()
+        assert np.all(np.abs(got - ref) <= 1e-5 * (np.abs(ref).max() + 1.0)), (b, t)
+        want = OI.topk_select(got.astype(np.float64)[None], top_k)[0]
+        assert np.array_equal(idx[b, t].cpu().numpy().astype(np.int64), want), (b, t)
