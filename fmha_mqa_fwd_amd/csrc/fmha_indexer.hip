@@ -110,22 +110,32 @@ void score_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 
   const int k_lane = l32 * KS + 16 * hlf;
   auto compute = [&](int t, const char* buf) __attribute__((always_inline)) {
+    constexpr int NKB = IDX_KT / 32;
     const int e0 = (tile0 + t) * IDX_KT;
+    // all NKB x NHB accumulators at once: independent MFMA chains, each K
+    // fragment read once for every head block
+    f32x16 s[NKB][NHB];
 #pragma unroll
-    for (int kb = 0; kb < IDX_KT / 32; ++kb) {
-      float acc = 0.f;
+    for (int cs = 0; cs < NCS; ++cs) {
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        f32x16 s = {};
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(buf + k_lane + kb * 32 * KS + cs * 32);
 #pragma unroll
-        for (int cs = 0; cs < NCS; ++cs) {
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(buf + k_lane + kb * 32 * KS + cs * 32);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[hb][cs], b, s, 0, 0, 0);
+        for (int hb = 0; hb < NHB; ++hb) {
+          const f32x16 zero = {};
+          s[kb][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[hb][cs], b,
+                                                              cs == 0 ? zero : s[kb][hb], 0, 0, 0);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc = fmaf(wr[hb][r], fmaxf(s[r], 0.f), acc);
       }
-      acc = pair_sum(acc);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float a[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[r & 3] = fmaf(wr[hb][r], fmaxf(s[kb][hb][r], 0.f), a[r & 3]);
+      const float acc = pair_sum((a[0] + a[1]) + (a[2] + a[3]));
       const int e = e0 + kb * 32 + l32;
       if (live && hlf == 0 && e < P) scores[(int64_t)token * P + e] = acc;
     }
