@@ -134,7 +134,8 @@ class SourcesCase:
     into fp32 partials, then the LSE merge (the composition fwd_sources runs),
     with every launch's arguments marshalled once."""
 
-    def __init__(self, dev, B=32, n_h=64, hd=512, top_k=512, pool=32768, window=128):
+    def __init__(self, dev, B=32, n_h=64, hd=512, top_k=512, pool=32768, window=128,
+                 splits=(8, 4)):
         import fmha_mqa_fwd_amd as F
 
         top = W.make_custom(B=B, T=1, n_h=n_h, hd=hd, s_k=top_k, pool=pool, out_dtype="bf16",
@@ -150,10 +151,13 @@ class SourcesCase:
         self.lse_parts = torch.empty((2, B, 1, n_h), dtype=torch.float32, device=dev)
         self.out = torch.empty((B, 1, n_h, hd), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, 1, n_h), dtype=torch.float32, device=dev)
+        # one token per sequence leaves a source's rows few: split its keys so
+        # that each launch fills the chip (each split forward merges its own
+        # partials, then the two sources are merged)
         self.plans = [F.FwdPlan(self.q, kp, vp, idx, scale=top.scale, out_dtype=torch.float32,
-                                out=self.parts[0], lse=self.lse_parts[0]),
+                                num_splits=splits[0], out=self.parts[0], lse=self.lse_parts[0]),
                       F.FwdPlan(self.q, kw, vw, None, scale=top.scale, out_dtype=torch.float32,
-                                out=self.parts[1], lse=self.lse_parts[1])]
+                                num_splits=splits[1], out=self.parts[1], lse=self.lse_parts[1])]
         lib = F._binding._lib
         self._merge = lib.fmha_lse_merge
         self._margs = (self.parts.data_ptr(), self.lse_parts.data_ptr(), 2, rows, hd,
@@ -165,7 +169,8 @@ class SourcesCase:
                       + 2 * B * window * hd * 2 + rows * hd * 2 + rows * 4)
         self.flops = 4 * rows * (top_k + window) * hd
         self.desc = (f"decode over two sources: B={B} T=1 n_h={n_h} hd={hd}, top-k {top_k} of "
-                     f"{pool} pool rows + {window}-key window, bf16 out")
+                     f"{pool} pool rows ({splits[0]} splits) + {window}-key window ({splits[1]} "
+                     f"splits), bf16 out")
 
     def __call__(self):
         for plan in self.plans:

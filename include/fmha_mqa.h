@@ -57,8 +57,9 @@ typedef enum {
 typedef enum { FMHA_F32 = 0, FMHA_BF16 = 1 } fmha_dtype;
 
 /* Bytes of workspace fmha_mqa_fwd needs for num_splits > 1 (0 when
- * num_splits == 1): fp32 partial outputs [num_splits, B*T*n_h, hd] and fp32
- * partial LSEs [num_splits, B*T*n_h], each region 256-byte aligned.
+ * num_splits == 1): partial outputs [num_splits, B*T*n_h, hd] sized for fp32
+ * (they are stored as bf16 when the output is bf16, in the same region) and
+ * fp32 partial LSEs [num_splits, B*T*n_h], each region 256-byte aligned.
  * Returns 0 as well for invalid arguments. */
 size_t fmha_mqa_workspace_bytes(int B, int T, int n_h, int hd, int num_splits);
 
@@ -72,7 +73,7 @@ size_t fmha_mqa_workspace_bytes(int B, int T, int n_h, int hd, int num_splits);
  *  out      [B, T, n_h, hd] of out_dtype (FMHA_F32 or FMHA_BF16, RNE rounding)
  *  lse      fp32 [B, T, n_h], natural log
  *  B, T, n_h >= 0 (a zero gives an immediate FMHA_OK); s_k >= 0 (0: every row
- *           empty, k/v/kv_idx may be NULL); hd in {64, 128, 256};
+ *           empty, k/v/kv_idx may be NULL); hd in {64, 128, 256, 512};
  *  pool_rows  rows of the k/v pools (gather only; ignored when kv_idx == NULL)
  *  scale    finite and > 0 (e.g. 1/sqrt(hd))
  *  num_splits  1: one pass over the keys.  > 1 (at most max(s_k, 1)): split-KV —
