@@ -158,6 +158,23 @@ def test_gather_out_of_range_indices_are_masked(F):
     assert torch.all(out[0, 2] == 0) and torch.all(torch.isneginf(lse[0, 2]))
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_gather_repeated_indices_count_each_time(F, splits):
+    """A pool row listed several times is several keys (each takes its own
+    softmax weight), as in the oracle's definition; a list of one repeated
+    row gives that row's V exactly."""
+    w = W.make_custom(B=1, T=3, n_h=64, hd=128, s_k=256, pool=512, out_dtype="f32", seed=23)
+    q, k, v, idx = W.make_inputs(w)
+    rep = idx.clone()
+    rep[0, 0, 128:] = rep[0, 0, :128]        # every row twice
+    rep[0, 1, ::2] = 7                       # row 7 on half the keys
+    rep[0, 2, :] = 11                        # one row only
+    out, lse = _run(F, q, k, v, rep, w.scale, torch.float32, splits)
+    _check(out, lse, q, k, v, rep, w.scale)
+    row = v[11].float()
+    assert torch.allclose(out[0, 2].cpu(), row.expand(64, -1), atol=1e-5)
+
+
 # ---------------------------------------------------- structure / adversarial
 def test_structured_inputs_catch_layout_swaps(F):
     """Distinct, smooth values per (key, d) and per head: any swapped axis or
