@@ -87,6 +87,23 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _same_gpu(dev: torch.device, **tensors) -> None:
+    """Every given tensor lives on the GPU `dev` (a host pointer or another
+    device's memory must never reach a kernel)."""
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {dev}")
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _check_buf(name: str, t: torch.Tensor, shape, dtypes) -> None:
+    """A caller-provided output: exactly `shape`, one of `dtypes`, contiguous."""
+    if tuple(t.shape) != tuple(shape) or t.dtype not in dtypes or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {'/'.join(str(d) for d in dtypes)} "
+                         f"tensor of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
 def default_scale(hd: int) -> float:
     """1/sqrt(hd) as the fp32 value the kernel receives."""
     return float(torch.tensor(1.0 / math.sqrt(hd), dtype=torch.float32))
@@ -134,6 +151,13 @@ class FwdPlan:
             if sink.dtype != torch.float32 or sink.shape != (n_h,) or not sink.is_contiguous():
                 raise ValueError("sink must be a contiguous float32 [n_h] tensor")
         dev = q.device
+        _same_gpu(dev, k=k, v=v, kv_idx=kv_idx, sink=sink, out=out, lse=lse, workspace=workspace)
+        if out is not None:
+            _check_buf("out", out, (B, T, n_h, hd), (torch.float32, torch.bfloat16))
+        if lse is not None:
+            _check_buf("lse", lse, (B, T, n_h), (torch.float32,))
+        if workspace is not None and not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
         if scale is None:
             scale = default_scale(hd)
         if out is None:
@@ -199,6 +223,11 @@ def fwd_sources(q: torch.Tensor, sources, scale: Optional[float] = None,
     if n < 1:
         raise ValueError("at least one key source is needed")
     dev = q.device
+    _same_gpu(dev, sink=sink, out=out, lse=lse)
+    if out is not None:
+        _check_buf("out", out, (B, T, n_h, hd), (torch.float32, torch.bfloat16))
+    if lse is not None:
+        _check_buf("lse", lse, (B, T, n_h), (torch.float32,))
     rows = B * T * n_h
     parts = torch.empty((n, B, T, n_h, hd), dtype=torch.float32, device=dev)
     lse_parts = torch.empty((n, B, T, n_h), dtype=torch.float32, device=dev)
@@ -229,6 +258,7 @@ def apply_sink(out: torch.Tensor, lse: torch.Tensor, sink: torch.Tensor, stream=
         raise ValueError("sink must be a contiguous float32 [n_h] tensor")
     if lse.dtype != torch.float32 or not (out.is_contiguous() and lse.is_contiguous()):
         raise ValueError("out and lse must be contiguous; lse float32")
+    _same_gpu(out.device, lse=lse, sink=sink)
     st = _lib.fmha_attention_sink(_ptr(out), _ptr(lse), _ptr(sink), lse.numel(), n_h, hd,
                                   _dtype_code(out.dtype), _stream_handle(stream))
     if st != 0:
@@ -249,6 +279,11 @@ def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
         raise ValueError("partials must be contiguous")
     P, R, hd = o_parts.shape
     dev = o_parts.device
+    _same_gpu(dev, lse_parts=lse_parts, out=out, lse=lse)
+    if out is not None:
+        _check_buf("out", out, (R, hd), (torch.float32, torch.bfloat16))
+    if lse is not None:
+        _check_buf("lse", lse, (R,), (torch.float32,))
     if out is None:
         out = torch.empty((R, hd), dtype=out_dtype, device=dev)
     if lse is None:
@@ -272,6 +307,9 @@ def index_scores(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor,
         raise ValueError("q, k and w must be contiguous")
     B, T, H, c = q.shape
     P = k.shape[0]
+    _same_gpu(q.device, k=k, w=w, scores=scores)
+    if scores is not None:
+        _check_buf("scores", scores, (B, T, P), (torch.float32,))
     if scores is None:
         scores = torch.empty((B, T, P), dtype=torch.float32, device=q.device)
     st = _lib.fmha_index_scores(_ptr(q), _ptr(k), _ptr(w), _ptr(scores), B, T, H, c, P,
@@ -287,8 +325,13 @@ def topk_select(scores: torch.Tensor, top_k: int, idx: Optional[torch.Tensor] = 
     [..., top_k] (ascending ids, -1 padding)."""
     if scores.dtype != torch.float32 or not scores.is_contiguous():
         raise ValueError("scores must be contiguous float32")
+    if scores.dim() < 1:
+        raise ValueError("scores must be [..., P]")
     P = scores.shape[-1]
     rows = scores.numel() // P if P else 0
+    _same_gpu(scores.device, idx=idx)
+    if idx is not None:
+        _check_buf("idx", idx, (*scores.shape[:-1], top_k), (torch.int32,))
     if idx is None:
         idx = torch.empty((*scores.shape[:-1], top_k), dtype=torch.int32, device=scores.device)
     st = _lib.fmha_topk_select(_ptr(scores), _ptr(idx), rows, P, int(top_k),

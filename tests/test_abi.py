@@ -175,10 +175,49 @@ def test_index_scores_validates(F, args, status):
     ((A, A, 4, 0, 8, None), 1),
     ((A, A, 4, 100, 0, None), 1),
     ((A, A, -1, 100, 8, None), 1),
-    ((A, A, 4, 40000, 8, None), 2),     # row longer than the LDS selection holds
+    ((A, A, 4, 40000, 8, None), 2),     # row longer than the 32768 keys one workgroup holds
     ((None, A, 4, 100, 8, None), 1),
     ((A, A + 2, 4, 100, 8, None), 3),
     ((None, None, 0, 100, 8, None), 0),
 ])
 def test_topk_select_validates(F, args, status):
     assert F._binding._lib.fmha_topk_select(*args) == status
+
+
+# ------------------------------------------------------- Python-side checks
+# Host tensors and wrong caller buffers are rejected before any device call,
+# so these run without a GPU.
+def test_wrappers_reject_host_tensors(F):
+    import torch
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        F.fwd(q, k, k.clone())
+    with pytest.raises(ValueError, match="GPU"):
+        F.FwdPlan(q, k, k.clone(), num_splits=2)
+    with pytest.raises(ValueError, match="GPU"):
+        F.lse_merge(torch.zeros(2, 3, 8), torch.zeros(2, 3))
+    with pytest.raises(ValueError, match="GPU"):
+        F.apply_sink(torch.zeros(3, 4, 8), torch.zeros(3, 4), torch.zeros(4))
+    with pytest.raises(ValueError, match="GPU"):
+        F.index_scores(torch.zeros(1, 1, 32, 64, dtype=torch.bfloat16),
+                       torch.zeros(5, 64, dtype=torch.bfloat16), torch.zeros(1, 1, 32))
+    with pytest.raises(ValueError, match="GPU"):
+        F.topk_select(torch.zeros(2, 100), 8)
+    with pytest.raises(ValueError, match="GPU"):
+        F.fwd_sources(q, [(k, k.clone(), None)])
+
+
+def test_device_and_buffer_checks(F):
+    import torch
+    B = F._binding
+    gpu = torch.device("cuda", 0)
+    with pytest.raises(ValueError, match="is on cpu"):
+        B._same_gpu(gpu, out=torch.zeros(3))
+    B._same_gpu(gpu, out=None)  # absent tensors are fine
+    good = torch.zeros(2, 3, 4, 8)
+    B._check_buf("out", good, (2, 3, 4, 8), (torch.float32,))
+    for bad in (torch.zeros(2, 3, 4, 9), torch.zeros(2, 3, 4, 8, dtype=torch.float64),
+                torch.zeros(2, 3, 8, 4).transpose(2, 3)):
+        with pytest.raises(ValueError, match="out must be"):
+            B._check_buf("out", bad, (2, 3, 4, 8), (torch.float32,))
