@@ -175,6 +175,32 @@ def test_gather_repeated_indices_count_each_time(F, splits):
     assert torch.allclose(out[0, 2].cpu(), row.expand(64, -1), atol=1e-5)
 
 
+@pytest.mark.parametrize("hd,gather", [(64, False), (128, False), (256, False), (512, False),
+                                       (128, True), (256, True)])
+def test_bf16_output_is_the_fp32_output_rounded_to_nearest_even(F, hd, gather):
+    """The bf16 epilogue rounds the same fp32 values the fp32 epilogue stores,
+    to nearest-even (torch's fp32 -> bf16 conversion is round-to-nearest-even)."""
+    w = W.make_custom(B=2, T=3, n_h=64, hd=hd, s_k=300, pool=2048 if gather else 0,
+                      out_dtype="f32", seed=31 + hd)
+    q, k, v, idx = W.make_inputs(w)
+    o32, l32 = _run(F, q, k, v, idx, w.scale, torch.float32, 1)
+    o16, l16 = _run(F, q, k, v, idx, w.scale, torch.bfloat16, 1)
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(l16, l32)
+
+
+def test_merge_bf16_output_is_its_fp32_output_rounded_to_nearest_even(F):
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(41)
+    parts = torch.randn(5, 300, 128, generator=g).to(dev)
+    lses = (torch.randn(5, 300, generator=g) * 3).to(dev)
+    o32, l32 = F.lse_merge(parts, lses, torch.float32)
+    o16, l16 = F.lse_merge(parts, lses, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(l16, l32)
+
+
 # ---------------------------------------------------- structure / adversarial
 def test_structured_inputs_catch_layout_swaps(F):
     """Distinct, smooth values per (key, d) and per head: any swapped axis or
