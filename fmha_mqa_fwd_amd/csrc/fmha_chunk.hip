@@ -98,7 +98,7 @@ void chunk_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: DMA guards and M0
   const int l32 = lane & 31;
   const int hlf = lane >> 5;
 
