@@ -324,6 +324,22 @@ def test_hd512_flash_sparse_topk(F):
     _case(F, w, rows=_sample_rows(w.rows, 640, 6))
 
 
+def test_hd512_decode_benchmarked_size_sampled(F):
+    """The hd 512 decode row as bench.py times it: B=32, 128 heads, s_k=1024,
+    8 splits, bf16 out (rows sampled)."""
+    w = W.make_custom(B=32, T=1, n_h=128, hd=512, s_k=1024, out_dtype="bf16", num_splits=8,
+                      seed=515)
+    _case(F, w, rows=_sample_rows(w.rows, 382, 7))
+
+
+def test_hd512_flash_topk_benchmarked_size_sampled(F):
+    """The hd 512 Flash top-k row as bench.py times it: B=4, T=512, 64 heads,
+    top-k 512 of a 32768-row pool, bf16 out (rows sampled)."""
+    w = W.make_custom(B=4, T=512, n_h=64, hd=512, s_k=512, pool=32768, out_dtype="bf16",
+                      seed=516)
+    _case(F, w, rows=_sample_rows(w.rows, 254, 8))
+
+
 @pytest.mark.parametrize("splits,out_dtype", [(1, "f32"), (3, "f32"), (2, "bf16")])
 def test_hd512_dense_prefill(F, splits, out_dtype):
     w = W.make_custom(B=1, T=40, n_h=8, hd=512, s_k=700, out_dtype=out_dtype, num_splits=splits,
