@@ -96,7 +96,9 @@ void fwd_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: DMA guards and M0
+  // scalar (DMA guards and M0 in scalar code) where it measured faster: not
+  // with the head dim split over waves, whose register pressure it raises
+  const int wave = DSPLIT == 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int l32 = lane & 31;
   const int hlf = lane >> 5;
 
