@@ -128,6 +128,21 @@ class Case:
         self.plan()
 
 
+class FloorCase:
+    """The gather-only floor of a gather workload: fmha_gather_floor reads the
+    same K/V rows for the same index lists with no attention arithmetic."""
+
+    def __init__(self, case):
+        self.F = case.F
+        self.k, self.v, self.idx = case.k, case.v, case.idx
+        w = case.w
+        self.out = torch.empty((w.B, w.T), dtype=torch.int32, device=case.k.device)
+        self.bytes = 2 * w.B * w.T * w.s_k * w.hd * 2  # K and V rows, gathered
+
+    def __call__(self):
+        self.F.gather_floor(self.k, self.v, self.idx, out=self.out)
+
+
 class SourcesCase:
     """Decode over two key sources — top-k rows gathered from a compressed
     pool plus a dense sliding window — in one softmax: one forward per source
@@ -303,7 +318,7 @@ def _busy_counters(d):
             by[kname][disp]["_dur"] = dur
     res = {}
     for k, disps in by.items():
-        clk, mfma = [], []
+        clk, mfma, flops = [], [], []
         for c in disps.values():
             g = c.get("GRBM_GUI_ACTIVE")
             # the dispatch timestamps are too coarse for short kernels
@@ -311,10 +326,17 @@ def _busy_counters(d):
                 clk.append(g / N_XCD / c["_dur"] / 1e9)
                 if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
                     mfma.append(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * g / N_XCD))
-        if clk:
-            res[k] = {"effective_clock_GHz": round(sorted(clk)[len(clk) // 2], 3)}
+            if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+                # bf16 matrix FLOPs the dispatch executed (512 per counted op)
+                flops.append(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512)
+        if clk or flops:
+            res[k] = {}
+            if clk:
+                res[k]["effective_clock_GHz"] = round(sorted(clk)[len(clk) // 2], 3)
             if mfma:
                 res[k]["mfma_busy_frac"] = round(sorted(mfma)[len(mfma) // 2], 4)
+            if flops:
+                res[k]["mfma_flops_per_launch"] = sorted(flops)[len(flops) // 2]
     return res
 
 
@@ -514,6 +536,16 @@ def main():
         print(f"[bench] {name}: {t['ms'] * 1e3:.1f} us/call flushed "
               f"({t['ms_warm'] * 1e3:.1f} warm), {t['tflops']:.1f} TFLOP/s, "
               f"{t['gbps']:.0f} GB/s", file=sys.stderr, flush=True)
+        if case.idx is not None:
+            # the memory side's floor for the same gathered rows
+            fl = FloorCase(case)
+            tf = time_case(fl, args.steps, args.warmup, flush_buf)
+            t["floor_ms"], t["floor_ms_warm"] = tf["ms"], tf["ms_warm"]
+            t["floor_gbps"] = fl.bytes / (tf["ms"] * 1e-3) / 1e9
+            print(f"[bench] {name} gather-only floor: {tf['ms'] * 1e3:.1f} us/call flushed "
+                  f"({tf['ms_warm'] * 1e3:.1f} warm), {t['floor_gbps']:.0f} GB/s gathered",
+                  file=sys.stderr, flush=True)
+            del fl
         del case
         torch.cuda.empty_cache()
 
@@ -584,6 +616,9 @@ def main():
         "sparse_topk": {"value": round(s["tflops"], 2), "unit": "TFLOP/s",
                         "frac_of_mfma_peak": round(s["tflops"] / PEAK_BF16_TFLOPS, 4),
                         "gathered_GBps": round(s["gbps"], 1),
+                        "gather_floor_us": round(s["floor_ms"] * 1e3, 2),
+                        "gather_floor_us_warm": round(s["floor_ms_warm"] * 1e3, 2),
+                        "gather_floor_GBps": round(s["floor_gbps"], 1),
                         "us_per_call": round(s["ms"] * 1e3, 2),
                         "us_per_call_warm": round(s["ms_warm"] * 1e3, 2),
                         "workload": s["workload"]},

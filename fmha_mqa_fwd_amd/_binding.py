@@ -37,6 +37,8 @@ SIGNATURES = {
     "fmha_index_scores": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                    _c_int, _c_int, _c_int, _c_void_p]),
     "fmha_topk_select": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p]),
+    "fmha_gather_floor": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                   _c_int, _c_int, _c_int, _c_void_p]),
     "fmha_status_string": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -345,6 +347,30 @@ def indexer_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, top_k: int,
                  stream=None) -> torch.Tensor:
     """kv_idx int32 [B, T, top_k] for fwd: the index scores, then the top-k."""
     return topk_select(index_scores(q, k, w, stream=stream), top_k, stream=stream)
+
+
+def gather_floor(k: torch.Tensor, v: torch.Tensor, kv_idx: torch.Tensor,
+                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fmha_gather_floor (a measurement helper): reads every gathered K and V
+    row of pools k, v [P, hd] for kv_idx [B, T, s_k]; returns the per-token XOR
+    of the words read, int32 [B, T] (the uint32 bit patterns)."""
+    if k.dim() != 2 or v.shape != k.shape or kv_idx.dim() != 3:
+        raise ValueError("k, v must be [P, hd] pools and kv_idx [B, T, s_k]")
+    if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16 or kv_idx.dtype != torch.int32:
+        raise ValueError("k, v must be bfloat16 and kv_idx int32")
+    if not (k.is_contiguous() and v.is_contiguous() and kv_idx.is_contiguous()):
+        raise ValueError("k, v and kv_idx must be contiguous")
+    B, T, s_k = kv_idx.shape
+    _same_gpu(k.device, v=v, kv_idx=kv_idx, out=out)
+    if out is not None:
+        _check_buf("out", out, (B, T), (torch.int32,))
+    if out is None:
+        out = torch.empty((B, T), dtype=torch.int32, device=k.device)
+    st = _lib.fmha_gather_floor(_ptr(k), _ptr(v), _ptr(kv_idx), _ptr(out), B, T, s_k, k.shape[1],
+                                k.shape[0], _stream_handle(stream))
+    if st != 0:
+        raise FmhaError("fmha_gather_floor", st)
+    return out
 
 
 def raw_fwd(*args) -> int:

@@ -23,7 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libfmha_mqa.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["api.hip", "fmha_fwd.hip", "fmha_chunk.hip", "lse_merge.hip", "fmha_indexer.hip"]
+SOURCES = ["api.hip", "fmha_fwd.hip", "fmha_chunk.hip", "lse_merge.hip", "fmha_indexer.hip",
+           "gather_floor.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are kept out of the generated code on purpose; the

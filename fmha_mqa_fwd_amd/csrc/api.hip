@@ -182,6 +182,24 @@ int fmha_topk_select(const float* scores, int32_t* idx, int rows, int P, int top
       fmha::launch_topk(scores, idx, rows, P, top_k, static_cast<hipStream_t>(stream)));
 }
 
+int fmha_gather_floor(const void* k, const void* v, const int32_t* kv_idx, uint32_t* out,
+                      int B, int T, int s_k, int hd, int pool_rows, void* stream) {
+  if (B < 0 || T < 0 || s_k < 0 || pool_rows < 1) return FMHA_ERR_INVALID_ARG;
+  if (hd != 64 && hd != 128 && hd != 256 && hd != 512) return FMHA_ERR_UNSUPPORTED;
+  const int64_t tokens = (int64_t)B * T;
+  if (tokens == 0) return FMHA_OK;
+  if (tokens > INT32_MAX || (int64_t)pool_rows * hd * 2 > INT32_MAX ||
+      (int64_t)s_k * hd * 2 / 16 > INT32_MAX)
+    return FMHA_ERR_UNSUPPORTED;
+  if (!k || !v || !kv_idx || !out) return FMHA_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(kv_idx, 4) || !aligned(out, 4))
+    return FMHA_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return launch_status(fmha::launch_gather_floor(
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), kv_idx, out, (int)tokens,
+      s_k, hd, pool_rows, static_cast<hipStream_t>(stream)));
+}
+
 int fmha_lse_merge(const float* o_parts, const float* lse_parts, int n_parts, int rows, int hd,
                    void* out, int out_dtype, float* lse, void* stream) {
   if (out_dtype != FMHA_F32 && out_dtype != FMHA_BF16) return FMHA_ERR_INVALID_ARG;

@@ -77,6 +77,10 @@ hipError_t launch_index_scores(const uint16_t* q, const uint16_t* k, const float
                                float* scores, int tokens, int H, int C, int P,
                                hipStream_t stream);
 int topk_max_pool();
+// gather_floor.hip: every gathered K and V row read once, no arithmetic
+hipError_t launch_gather_floor(const uint16_t* k, const uint16_t* v, const int32_t* idx,
+                               uint32_t* out, int tokens, int s_k, int hd, int pool_rows,
+                               hipStream_t stream);
 hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int P, int top_k,
                        hipStream_t stream);
 

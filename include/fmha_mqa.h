@@ -116,6 +116,17 @@ int fmha_mqa_fwd_sink(const void* q, const void* k, const void* v,
 int fmha_attention_sink(void* out, float* lse, const float* sink, int rows,
                         int n_h, int hd, int out_dtype, void* stream);
 
+/* Measurement helper, not part of the attention: the gather-only floor of the
+ * top-k row gather (the data movement the gathered attention cannot avoid:
+ * token (b, t) reads pool rows kv_idx[b, t, 0..s_k-1] of k and of v, every
+ * 16-byte chunk once, with no arithmetic on them).  Writes the XOR of all words
+ * a token read to out[b*T + t] (so no load can be dropped; an entry outside
+ * [0, pool_rows) reads nothing).
+ *  k, v   bf16 pools [pool_rows, hd], hd in {64, 128, 256, 512}, 16-byte aligned
+ *  kv_idx int32 [B, T, s_k];  out uint32 [B*T], 4-byte aligned. */
+int fmha_gather_floor(const void* k, const void* v, const int32_t* kv_idx, uint32_t* out,
+                      int B, int T, int s_k, int hd, int pool_rows, void* stream);
+
 /* Log-sum-exp merge of normalised partial results (page "CURRENT ISSUE: UMMA
  * FMHA — Full Pipeline + Production", "Next steps" 4):
  *   M = max_i lse_i,  w_i = exp(lse_i - M),

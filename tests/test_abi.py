@@ -31,10 +31,10 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["fmha_attention_sink", "fmha_index_scores",
-                                     "fmha_lse_merge", "fmha_mqa_fwd", "fmha_mqa_fwd_sink",
-                                     "fmha_mqa_workspace_bytes", "fmha_status_string",
-                                     "fmha_topk_select"]
+    assert _declared_functions() == ["fmha_attention_sink", "fmha_gather_floor",
+                                     "fmha_index_scores", "fmha_lse_merge", "fmha_mqa_fwd",
+                                     "fmha_mqa_fwd_sink", "fmha_mqa_workspace_bytes",
+                                     "fmha_status_string", "fmha_topk_select"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -221,3 +221,15 @@ def test_device_and_buffer_checks(F):
                 torch.zeros(2, 3, 8, 4).transpose(2, 3)):
         with pytest.raises(ValueError, match="out must be"):
             B._check_buf("out", bad, (2, 3, 4, 8), (torch.float32,))
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, A, A, A, 1, 2, 64, 100, 0, None), 1),      # empty pool
+    ((A, A, A, A, 1, 2, 64, 96, 10, None), 2),      # head dim
+    ((A, A, A, A, -1, 2, 64, 128, 10, None), 1),
+    ((None, A, A, A, 1, 2, 64, 128, 10, None), 1),
+    ((A + 8, A, A, A, 1, 2, 64, 128, 10, None), 3),
+    ((None, None, None, None, 0, 2, 64, 128, 10, None), 0),  # no tokens: no-op
+])
+def test_gather_floor_validates(F, args, status):
+    assert F._binding._lib.fmha_gather_floor(*args) == status

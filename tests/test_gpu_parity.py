@@ -366,3 +366,27 @@ def test_lse_merge_entry_point(F, hd, out_dtype):
     assert m["max_abs"] <= (1e-2 if out_dtype == "bf16" else 1e-5), m
     assert m["lse_err"] <= 1e-5, m
     assert torch.all(out[10] == 0) and torch.isneginf(L[10])
+
+
+# ------------------------------------------------- measurement helper
+def test_gather_floor_reads_every_gathered_row(F):
+    """fmha_gather_floor (the sparse config's gather-only floor) reads each
+    listed K and V row once: its per-token XOR of the words read equals the
+    XOR computed on the CPU; masked entries read nothing."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(61)
+    P, hd, B, T, s_k = 500, 128, 2, 3, 100
+    k = torch.randn(P, hd, generator=g).to(torch.bfloat16)
+    v = torch.randn(P, hd, generator=g).to(torch.bfloat16)
+    idx = torch.randint(0, P, (B, T, s_k), generator=g, dtype=torch.int32)
+    idx[0, 1, 7] = -1
+    idx[1, 2, :10] = P + 3
+    got = F.gather_floor(k.to(dev), v.to(dev), idx.to(dev)).cpu().numpy().view(np.uint32)
+    kw = k.view(torch.int32).numpy().view(np.uint32)   # [P, hd/2] words
+    vw = v.view(torch.int32).numpy().view(np.uint32)
+    for b in range(B):
+        for t in range(T):
+            rows = idx[b, t].numpy()
+            rows = rows[(rows >= 0) & (rows < P)]
+            want = np.bitwise_xor.reduce(np.concatenate([kw[rows].ravel(), vw[rows].ravel()]))
+            assert got[b, t] == want, (b, t)
