@@ -487,3 +487,45 @@ def test_planted_oracle_mistakes_are_caught(name, monkeypatch):
         except AssertionError:
             caught += 1
     assert caught >= 1, f"mutant {name} passed every pin"
+
+
+# Plausible misreadings of the multi-source oracle: each must fail a sources pin.
+def _source_mutants():
+    good = oracle.fp64.attention_sources
+
+    def first_source_only(q, sources, scale, rows=None, sink=None):
+        return good(q, sources[:1], scale, rows=rows, sink=sink)
+
+    def mean_of_sources(q, sources, scale, rows=None, sink=None):
+        outs = [good(q, [s], scale, rows=rows, sink=sink) for s in sources]
+        return (sum(o for o, _ in outs) / len(outs),
+                np.log(sum(np.exp(l) for _, l in outs)))
+
+    def window_of_batch_zero(q, sources, scale, rows=None, sink=None):
+        fixed = []
+        for k, v, i in sources:
+            if i is None:  # a dense source read from batch 0 for every batch
+                k = np.repeat(np.asarray(k, np.float64)[:1], k.shape[0], axis=0)
+                v = np.repeat(np.asarray(v, np.float64)[:1], v.shape[0], axis=0)
+            fixed.append((k, v, i))
+        return good(q, fixed, scale, rows=rows, sink=sink)
+
+    return {"first_source_only": first_source_only, "mean_of_sources": mean_of_sources,
+            "window_of_batch_zero": window_of_batch_zero}
+
+
+@pytest.mark.parametrize("name", sorted(_source_mutants()))
+def test_planted_source_mistakes_are_caught(name, monkeypatch):
+    import oracle.fp64 as A
+
+    mutant = _source_mutants()[name]  # wraps the correct function, taken before patching
+    monkeypatch.setattr(A, "attention_sources", mutant)
+    monkeypatch.setattr(oracle, "attention_sources", mutant)
+    caught = 0
+    for pin in (test_sources_match_brute_force_over_the_concatenated_keys,
+                test_sources_equal_the_merge_of_each_source):
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"mutant {name} passed every sources pin"
