@@ -320,6 +320,222 @@ void fwd_kernel(FwdParams p) {
   w.store(p, grow0, row0, split, l32, hlf, col0, dh == 0);
 }
 
+// ------------------------------------------------------------------------
+// Gather kernel with a three-stage pipeline on unpadded, XOR-swizzled K/V
+// stages (16-byte chunk c of row r stored at chunk c ^ swz(r), so the operand
+// reads stay free of bank conflicts without pad bytes): a 32-key stage is
+// 32 x hd x 2 bytes per tensor.  Two workgroups share a CU (three would
+// spill registers: the swizzled operand addresses do not fold into immediate
+// offsets), each with two tiles in flight.  The DMA of tile t+2 streams while tile t is
+// computed; each tile ends with a wait that leaves only that newest DMA
+// outstanding, then a plain s_barrier.  The split's index list (validated)
+// is staged in LDS first, so the loop issues no global loads; the DMA is
+// issued from inline assembly so the compiler adds no waits of its own.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "{m0}"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
+  r[3] = BUF_FLAGS;
+  return r;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int CPR>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (CPR >= 16) return row & 15;
+  else return (row & 7) ^ ((row >> 3) & 1);
+}
+template <int CPR>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (CPR >= 16) return (0xCA60 >> (4 * (row & 3))) & 15;  // 0, 6, 10, 12
+  else return (0x2460 >> (4 * (row & 3))) & 15;                      // 0, 6, 4, 2
+}
+
+constexpr int GSW_MAX_KEYS = 1024;  // a split's index list held in LDS
+
+template <int HD, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void fwd_gather_sw_kernel(FwdParams p) {
+  constexpr int WAVES = 4, QW = 32, KT = 32, NKB = 1, NKS = 2;
+  constexpr int M_WG = WAVES * QW;
+  constexpr int ROW = HD * 2;                  // bytes per row (unpadded)
+  constexpr int CPR = ROW / 16;                // 16-byte chunks per row
+  constexpr int STAGE = KT * ROW;              // bytes per tensor per stage
+  constexpr int NI = STAGE / 1024;             // DMA instructions per tensor per tile
+  static_assert(NI % WAVES == 0, "every wave issues the same DMA count");
+  constexpr int J = NI / WAVES;                // per wave per tensor
+  constexpr int PER_TILE = 2 * J;              // this wave's DMAs per tile (K and V)
+
+  __shared__ __attribute__((aligned(1024))) char sK0[STAGE], sK1[STAGE], sK2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sV0[STAGE], sV1[STAGE], sV2[STAGE];
+  __shared__ int sIdx[GSW_MAX_KEYS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hlf = lane >> 5;
+
+  int bid = blockIdx.x;
+  const int tile = bid % p.tiles_per_group;
+  bid /= p.tiles_per_group;
+  const int group = bid % p.n_groups;
+  const int split = bid / p.n_groups;
+
+  const int key_lo = split * p.chunk;
+  const int key_hi = min(key_lo + p.chunk, p.s_k);
+  const int nk = max(key_hi - key_lo, 0);  // <= GSW_MAX_KEYS (host guarantees)
+  const int n_tiles = (nk + KT - 1) / KT;
+  const int row0 = tile * M_WG + wave * QW;
+  const int64_t grow0 = (int64_t)group * p.rows_per_group;
+  const int32_t* ibase = p.kv_idx + (int64_t)group * p.s_k + key_lo;
+
+  // DMA geometry: instruction j of this wave fills stage bytes
+  // [1024 (wave + 4 j), +1024): lane -> (row, physical chunk)
+  int drow[J], dphys[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int pos = (wave + WAVES * j) * 1024 + lane * 16;
+    drow[j] = pos / ROW;
+    dphys[j] = (pos % ROW) / 16;
+  }
+  const u32x4 rk = buffer_rsrc(p.k, (uint32_t)p.pool_rows * ROW);
+  const u32x4 rv = buffer_rsrc(p.v, (uint32_t)p.pool_rows * ROW);
+  struct Offs {
+    uint32_t k[J], v[J];
+  };
+  // byte offsets of this lane's DMA chunks for tile t (OOB: masked key or past the end)
+  auto offsets = [&](int t) __attribute__((always_inline)) {
+    Offs o;
+    const bool live = t < n_tiles;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      o.k[j] = OOB;
+      o.v[j] = OOB;
+      if (live) {
+        const int idx = sIdx[t * KT + drow[j]];
+        if (idx >= 0) {
+          o.k[j] = (uint32_t)idx * ROW + 16u * (dphys[j] ^ swz_k<CPR>(drow[j]));
+          o.v[j] = (uint32_t)idx * ROW + 16u * (dphys[j] ^ swz_v<CPR>(drow[j]));
+        }
+      }
+    }
+    return o;
+  };
+  auto issue = [&](const Offs& o, char* kbuf, char* vbuf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int inst = wave + WAVES * j;
+      dma16(rk, (uint32_t)(uintptr_t)(kbuf + inst * 1024), o.k[j]);
+      dma16(rv, (uint32_t)(uintptr_t)(vbuf + inst * 1024), o.v[j]);
+    }
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  };
+
+  Rows<HD, QW> w;
+  w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf);
+  const float c = p.scale_log2;
+  const int jj = lane & 15;
+  const int dsub = (lane >> 4) & 1;
+  const int kx = swz_k<CPR>(l32);  // K operand row l32
+  Offs ahead;
+  uint64_t tile_masked = 0;  // bit t: tile t has a masked key
+
+  auto step = [&](int t, const char* kcur, const char* vcur, char* kfar, char* vfar)
+      __attribute__((always_inline)) {
+    issue(ahead, kfar, vfar);  // tile t+2
+    ahead = offsets(t + 3);
+    f32x16 s[NKB][1];
+    w.template qk<NKB>(s, [&](int, int ds) {
+      return *reinterpret_cast<const bf16x8*>(kcur + l32 * ROW + 16 * ((2 * ds + hlf) ^ kx));
+    });
+    const int kbase = t * KT;
+    if ((tile_masked >> t) & 1) {
+      w.template mask<NKB>(s, hlf, [&](int kk) { return sIdx[kbase + kk] >= 0; });
+    }
+    bf16x8 pf[1][NKS];
+    if (w.template softmax<NKB>(s, pf, c)) w.rescale_o();
+    w.template pv<NKS>(pf, [&](int ks, int db) {
+      const int r0 = 16 * ks + 4 * hlf + (jj >> 2);
+      const int r1 = r0 + 8;
+      const int ch = 4 * db + 2 * dsub + ((jj & 3) >> 1);
+      const int sub = 8 * (jj & 1);
+      return v_frag_tr(vcur + r0 * ROW + 16 * (ch ^ swz_v<CPR>(r0)) + sub,
+                       vcur + r1 * ROW + 16 * (ch ^ swz_v<CPR>(r1)) + sub);
+    });
+    // tile t+1 (issued a step ago) has landed; tile t+2 may still be in flight
+    wait_vmcnt<PER_TILE>();
+    barrier();
+  };
+
+  // the split's index list, validated, in LDS (keys past the split: masked)
+  for (int i = tid; i < n_tiles * KT; i += 256) {
+    int idx = -1;
+    if (i < nk) idx = ibase[i];
+    sIdx[i] = (idx >= 0 && idx < p.pool_rows) ? idx : -1;
+  }
+  // Q and the index list are in before any DMA is issued, so the compiler's
+  // own waits for them stay out of the loop
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int r = 0; r < n_tiles; r += 2) {  // each wave reads the list two tiles at a time
+    const int i = r * KT + lane;
+    const uint64_t b = __ballot(i < n_tiles * KT && sIdx[min(i, GSW_MAX_KEYS - 1)] < 0);
+    tile_masked |= (((uint32_t)b != 0) ? 1ull : 0ull) << r;
+    tile_masked |= (((uint32_t)(b >> 32) != 0) ? 1ull : 0ull) << (r + 1);
+  }
+  if (n_tiles > 0) {
+    issue(offsets(0), sK0, sV0);
+    issue(offsets(1), sK1, sV1);
+    ahead = offsets(2);
+    wait_vmcnt<PER_TILE>();  // tile 0 has landed
+    barrier();
+    for (int t = 0; t < n_tiles; t += 3) {
+      step(t, sK0, sV0, sK2, sV2);
+      if (t + 1 < n_tiles) step(t + 1, sK1, sV1, sK0, sV0);
+      if (t + 2 < n_tiles) step(t + 2, sK2, sV2, sK1, sV1);
+    }
+  }
+  // every DMA (also the zero-filling ones past the end) has landed and every
+  // wave is past its reads before the stages are reused for the epilogue
+  wait_vmcnt<0>();
+  barrier();
+  constexpr int RB_BF16 = HD * 2;
+  if constexpr (QW * RB_BF16 <= STAGE) {
+    if (is_bf16(p.out_mode)) {
+      char* const region = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sK2 : sV0;
+      w.store_lds(p, grow0, row0, split, lane, [&](int r) { return region + r * RB_BF16; });
+      return;
+    }
+  }
+  w.store(p, grow0, row0, split, l32, hlf);
+}
+
+template <int HD, int WPE>
+hipError_t launch_gather_sw(const FwdParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)p.tiles_per_group * p.n_groups * p.num_splits));
+  hipLaunchKernelGGL((fwd_gather_sw_kernel<HD, WPE>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 struct Shape {
   int qw, kt, waves, wpe;
   int rows() const { return waves * qw; }  // rows per workgroup (before a head-dim split)
@@ -371,7 +587,8 @@ hipError_t launch_fwd(FwdParams p, int hd, hipStream_t stream) {
       return gather ? launch_t<64, 32, 64, 4, 2, true>(p, stream)
                     : launch_t<64, 32, 32, 4, 3, false>(p, stream);
     case 128:
-      return gather ? launch_t<128, 32, 64, 4, 2, true>(p, stream)
+      return gather ? (p.chunk <= GSW_MAX_KEYS ? launch_gather_sw<128, 2>(p, stream)
+                                               : launch_t<128, 32, 64, 4, 2, true>(p, stream))
                     : launch_t<128, 32, 32, 4, 3, false>(p, stream);
     case 256:
       return gather ? launch_t<256, 32, 32, 4, 1, true>(p, stream)

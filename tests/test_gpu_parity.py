@@ -124,6 +124,15 @@ def test_gather(F, hd, n_h):
     _case(F, w)
 
 
+@pytest.mark.parametrize("s_k,splits", [(1024, 1), (1025, 1), (1500, 1), (1500, 2)])
+def test_gather_list_lengths_around_the_staged_limit(F, s_k, splits):
+    """A split of up to 1024 gathered keys runs the kernel that stages its
+    index list in LDS; longer splits run the other gather kernel."""
+    w = W.make_custom(B=1, T=3, n_h=128, hd=128, s_k=s_k, pool=4096, out_dtype="bf16",
+                      num_splits=splits, seed=s_k + splits)
+    _case(F, w)
+
+
 def test_gather_split(F):
     w = W.make_custom(B=2, T=3, n_h=128, hd=128, s_k=1024, pool=8192, out_dtype="bf16",
                       num_splits=4, seed=5)
