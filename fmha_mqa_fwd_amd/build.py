@@ -24,7 +24,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libfmha_mqa.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["api.hip", "fmha_fwd.hip", "fmha_chunk.hip", "lse_merge.hip", "fmha_indexer.hip",
-           "gather_floor.hip"]
+           "gather_floor.hip", "fmha_gather512.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are kept out of the generated code on purpose; the
@@ -35,6 +35,16 @@ COMMON_FLAGS = [
     "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]
+
+
+# Per-source additions: MFMA results in ordinary VGPRs.  In the kernels that
+# run at one wave per SIMD (head dim 256 and 512, the whole-chunk split
+# kernel) the compiler otherwise keeps O in accumulation registers and copies
+# it out and back on every tile for the (rare) rescale's multiplies; the
+# other kernels of these files compile to the same code either way.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+SOURCE_FLAGS = {"fmha_gather512.hip": _VGPR_FORM, "fmha_fwd.hip": _VGPR_FORM,
+                "fmha_chunk.hip": _VGPR_FORM}
 
 
 def _hipcc() -> str:
@@ -62,7 +72,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([hipcc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB_PATH + ".tmp"

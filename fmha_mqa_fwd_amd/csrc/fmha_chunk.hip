@@ -30,30 +30,6 @@ namespace {
 
 using namespace dev;
 
-template <int CPR>
-__device__ __forceinline__ int swz_k(int row) {
-  if constexpr (CPR >= 16) {
-    return row & 15;
-  } else {
-    return (row & 7) ^ ((row >> 3) & 1);
-  }
-}
-template <int CPR>
-__device__ __forceinline__ int swz_v(int row) {
-  if constexpr (CPR >= 16) {
-    return (0xCA60 >> (4 * (row & 3))) & 15;  // 0, 6, 10, 12
-  } else {
-    return (0x2460 >> (4 * (row & 3))) & 15;  // 0, 6, 4, 2
-  }
-}
-
-// s_waitcnt vmcnt(n) with the other counters left unconstrained (gfx9
-// encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in [15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 constexpr int CHUNK_LDS_BYTES = 64 * 1024;  // per tensor
 
 template <int HD>
@@ -199,10 +175,10 @@ void chunk_kernel(FwdParams p) {
     // have landed in LDS, a plain s_barrier publishes every wave's share.  (A
     // __syncthreads() would add a release fence, i.e. wait for all of them.)
     switch (g) {  // g is unrolled away; the wait needs an immediate count
-      case 0: wait_vm<2 * IPW * (NGROUP - 1)>(); break;
-      case 1: wait_vm<2 * IPW * (NGROUP - 2)>(); break;
-      case 2: wait_vm<2 * IPW * (NGROUP - 3)>(); break;
-      default: wait_vm<0>(); break;
+      case 0: wait_vmcnt<2 * IPW * (NGROUP - 1)>(); break;
+      case 1: wait_vmcnt<2 * IPW * (NGROUP - 2)>(); break;
+      case 2: wait_vmcnt<2 * IPW * (NGROUP - 3)>(); break;
+      default: wait_vmcnt<0>(); break;
     }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");

@@ -388,6 +388,55 @@ struct Rows {
   }
 };
 
+// ---- K/V movement by LDS-DMA (buffer_load_dwordx4 ... lds): each lane's 16
+// bytes land at M0 + 16*lane in LDS, no registers involved.
+
+constexpr uint32_t OOB = 0x80000000u;  // beyond any descriptor's byte count: reads zeros
+
+// One LDS-DMA instruction from inline assembly: the compiler tracks none of
+// these, so it inserts no completion waits of its own; the kernels wait with
+// wait_vmcnt.  M0 (the LDS destination) is the asm operand bound to m0.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "{m0}"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// Raw buffer descriptor over [base, base + nbytes): reads past the end return zeros.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
+  r[3] = BUF_FLAGS;
+  return r;
+}
+
+// s_waitcnt vmcnt(N) with the other counters left unconstrained (gfx9
+// encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// XOR swizzles of 16-byte chunks in unpadded LDS rows of CPR chunks: K uses
+// chunk ^ swz_k(row) so that the 16 rows one operand read touches at a column
+// land on distinct banks; V uses chunk ^ swz_v(row) for the 4-row x 64-byte
+// footprint of ds_read_b64_tr_b16.
+template <int CPR>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (CPR >= 16) return row & 15;
+  else return (row & 7) ^ ((row >> 3) & 1);
+}
+template <int CPR>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (CPR >= 16) return (0xCA60 >> (4 * (row & 3))) & 15;  // 0, 6, 10, 12
+  else return (0x2460 >> (4 * (row & 3))) & 15;                      // 0, 6, 4, 2
+}
+
 // A V fragment from two ds_read_b64_tr_b16 reads at byte addresses a0 (keys
 // e = 0..3) and a1 (keys e = 4..7) within LDS.
 __device__ __forceinline__ bf16x8 v_frag_tr(const char* a0, const char* a1) {

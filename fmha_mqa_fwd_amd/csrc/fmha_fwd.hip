@@ -54,7 +54,6 @@ struct Lds {
   static constexpr int V_STRIDE = ROW + 64;
 };
 
-constexpr uint32_t OOB = 0x80000000u;  // beyond any descriptor's byte count
 
 // Head dims above 256: DSPLIT = 2 waves share the same QW rows, each holding
 // half of the head dim (its Q^T columns, its O^T rows): each computes a
@@ -331,40 +330,6 @@ void fwd_kernel(FwdParams p) {
 // outstanding, then a plain s_barrier.  The split's index list (validated)
 // is staged in LDS first, so the loop issues no global loads; the DMA is
 // issued from inline assembly so the compiler adds no waits of its own.
-__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "{m0}"(lds_addr), "v"(voff), "s"(rsrc)
-               : "memory");
-}
-
-__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t nbytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  u32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
-  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
-  r[3] = BUF_FLAGS;
-  return r;
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-template <int CPR>
-__device__ __forceinline__ int swz_k(int row) {
-  if constexpr (CPR >= 16) return row & 15;
-  else return (row & 7) ^ ((row >> 3) & 1);
-}
-template <int CPR>
-__device__ __forceinline__ int swz_v(int row) {
-  if constexpr (CPR >= 16) return (0xCA60 >> (4 * (row & 3))) & 15;  // 0, 6, 10, 12
-  else return (0x2460 >> (4 * (row & 3))) & 15;                      // 0, 6, 4, 2
-}
-
 constexpr int GSW_MAX_KEYS = 1024;  // a split's index list held in LDS
 
 template <int HD, int WPE>
@@ -594,7 +559,8 @@ hipError_t launch_fwd(FwdParams p, int hd, hipStream_t stream) {
       return gather ? launch_t<256, 32, 32, 4, 1, true>(p, stream)
                     : launch_t<256, 32, 32, 4, 1, false>(p, stream);
     case 512:
-      return gather ? launch_t<512, 32, 32, 4, 1, true>(p, stream)
+      return gather ? (p.chunk <= gather512_max_keys() ? launch_gather512(p, stream)
+                                                       : launch_t<512, 32, 32, 4, 1, true>(p, stream))
                     : launch_t<512, 32, 32, 4, 1, false>(p, stream);
     default:
       return hipErrorInvalidValue;

@@ -1,0 +1,220 @@
+// Multi-query attention forward with the top-k row gather at head dim 512,
+// for gfx950.
+//
+// The shape is DeepSeek-V4's (page "May 24, 2026 — Session Start Plan", Key
+// Numbers and File Map: head dim 512, Flash 64 query heads over top_k 512
+// gathered keys, Pro 128 heads over top_k 1024): every query head of a token
+// attends to the same s_k pool rows, picked by kv_idx (dsv4/kernels/cuda
+// commit log, KV row gather).
+//
+// Work split, as in the streaming kernel's head-dim-512 form: four waves = two
+// blocks of 32 query rows x two halves of the head dim.  A wave holds its half
+// of Q^T and of O^T, computes S^T over its 256 columns, and the two partials
+// of a row block are summed through LDS before the (identical) softmax; each
+// wave then does PV for its half of O.
+//
+// K/V movement (what this kernel changes):
+//   * One LDS-DMA instruction moves one whole 1 KiB row.  M0 points at the
+//     row's padded LDS slot and lane l takes bytes 16l..16l+15, so a lane's
+//     offset is the row's pool offset + 16l, and the K and V instructions of a
+//     row share it.  The padding (K +16 bytes, V +64 bytes per row) keeps the
+//     operand reads free of bank conflicts with immediate offsets.
+//   * The split's index list is validated once and staged in LDS as pool byte
+//     offsets (OOB for an invalid entry or a key past the split: the row reads
+//     as zeros and its logit is masked).  A per-tile "has a masked key" bit
+//     lives in scalar registers.
+//   * Two K and two V stages.  K(t+2) is issued as soon as every wave is past
+//     QK^T(t) (the barrier of the S exchange), V(t+1) at the start of tile t;
+//     each tile ends with a wait that leaves K(t+2) in flight.  The DMA is
+//     issued from inline assembly, so the compiler adds no waits of its own.
+#include "fmha_device.h"
+
+namespace fmha {
+namespace {
+
+using namespace dev;
+
+constexpr int G5_HD = 512;
+constexpr int G5_MAX_KEYS = 1024;  // a split's index list held in LDS
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_gather512_kernel(FwdParams p) {
+  constexpr int HD = G5_HD, HDW = HD / 2, QW = 32, KT = 32, WAVES = 4, NKS = KT / 16;
+  constexpr int M_WG = 2 * QW;              // two row blocks
+  constexpr int ROW = HD * 2;               // bytes per K/V row
+  constexpr int KS = ROW + 16;              // padded LDS row strides
+  constexpr int VS = ROW + 64;
+  constexpr int RPW = KT / WAVES;           // rows each wave moves per tile and tensor
+  static_assert(ROW == 64 * 16, "one DMA instruction per row");
+
+  __shared__ __attribute__((aligned(16))) char sK0[KT * KS], sK1[KT * KS];
+  __shared__ __attribute__((aligned(16))) char sV0[KT * VS], sV1[KT * VS];
+  __shared__ __attribute__((aligned(16))) float sX[WAVES * 64 * 16];  // S^T partials
+  __shared__ __attribute__((aligned(16))) uint32_t sOff[G5_MAX_KEYS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hlf = lane >> 5;
+  const int dh = wave & 1;                  // which head-dim half this wave holds
+  const int col0 = dh * HDW;
+
+  int bid = blockIdx.x;
+  const int tile = bid % p.tiles_per_group;
+  bid /= p.tiles_per_group;
+  const int group = bid % p.n_groups;
+  const int split = bid / p.n_groups;
+
+  const int key_lo = split * p.chunk;
+  const int key_hi = min(key_lo + p.chunk, p.s_k);
+  const int nk = max(key_hi - key_lo, 0);  // <= G5_MAX_KEYS (host guarantees)
+  const int n_tiles = (nk + KT - 1) / KT;
+  const int row0 = tile * M_WG + (wave >> 1) * QW;
+  const int64_t grow0 = (int64_t)group * p.rows_per_group;
+  const int32_t* ibase = p.kv_idx + (int64_t)group * p.s_k + key_lo;
+
+  const u32x4 rk = buffer_rsrc(p.k, (uint32_t)p.pool_rows * ROW);
+  const u32x4 rv = buffer_rsrc(p.v, (uint32_t)p.pool_rows * ROW);
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+
+  // the split's index list, validated, as pool byte offsets
+  for (int i = tid; i < n_tiles * KT; i += 256) {
+    int idx = -1;
+    if (i < nk) idx = ibase[i];
+    sOff[i] = (idx >= 0 && idx < p.pool_rows) ? (uint32_t)idx * ROW : OOB;
+  }
+  Rows<HDW, QW, HD> w;
+  w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf, col0);
+  // Q and the list are in before any DMA is issued, so the compiler's own
+  // waits for them stay out of the loop
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  uint64_t tile_masked = 0;  // bit t: tile t has a masked key
+  for (int r = 0; r < n_tiles; r += 2) {  // each wave reads the list two tiles at a time
+    const int i = r * KT + lane;
+    const uint64_t b = __ballot(i < n_tiles * KT && sOff[min(i, G5_MAX_KEYS - 1)] == OOB);
+    tile_masked |= (((uint32_t)b != 0) ? 1ull : 0ull) << r;
+    tile_masked |= (((uint32_t)(b >> 32) != 0) ? 1ull : 0ull) << (r + 1);
+  }
+
+  // this lane's DMA offsets for the RPW rows this wave moves in tile t
+  // (rows RPW*wave .. +RPW-1); past the last tile every row reads as zeros
+  struct Offs {
+    uint32_t o[RPW];
+  };
+  auto offsets = [&](int t) __attribute__((always_inline)) {
+    Offs r;
+    if (t < n_tiles) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(sOff + t * KT + wave * RPW);
+#pragma unroll
+      for (int h = 0; h < RPW / 4; ++h) {
+        const u32x4 x = src[h];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.o[4 * h + e] = x[e] + lane16;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) r.o[j] = OOB;
+    }
+    return r;
+  };
+  auto issue = [&](const u32x4& rsrc, const Offs& o, char* buf, int stride)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+      dma16(rsrc, (uint32_t)(uintptr_t)(buf + (wave * RPW + j) * stride), o.o[j]);
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  };
+
+  const float c = p.scale_log2;
+  const int jj = lane & 15;
+  const int dsub = (lane >> 4) & 1;
+  // per-lane operand offsets within a stage (see fwd_kernel): K row l32,
+  // bytes 16*hlf of each 32-byte step; V rows/columns of the transposed read
+  const int k_lane = l32 * KS + 16 * hlf + 2 * col0;
+  const int v_lane = (4 * hlf + (jj >> 2)) * VS + 2 * (16 * dsub + 4 * (jj & 3)) + 2 * col0;
+  f32x4* const x_mine = reinterpret_cast<f32x4*>(sX + (wave * 64 + lane) * 16);
+  const f32x4* const x_theirs = reinterpret_cast<const f32x4*>(sX + ((wave ^ 1) * 64 + lane) * 16);
+
+  Offs next;  // offsets of tile t+1 (its K is in flight, its V is issued at the start of t)
+  auto step = [&](int t, char* kcur, const char* vcur, char* vnext)
+      __attribute__((always_inline)) {
+    issue(rv, next, vnext, VS);  // V(t+1)
+    f32x16 s[1][1];
+    w.template qk<1>(s, [&](int, int ds) {
+      return *reinterpret_cast<const bf16x8*>(kcur + k_lane + ds * 32);
+    });
+    // S^T = this wave's partial + its partner's (same lanes, same layout)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x_mine[i] = f32x4{s[0][0][4 * i], s[0][0][4 * i + 1], s[0][0][4 * i + 2], s[0][0][4 * i + 3]};
+    barrier();  // every wave is past QK^T(t): K(t)'s stage is free
+    const Offs ahead = offsets(t + 2);
+    issue(rk, ahead, kcur, KS);  // K(t+2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 o = x_theirs[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[0][0][4 * i + e] += o[e];
+    }
+    if ((tile_masked >> t) & 1) {
+      const int kbase = t * KT;
+      w.template mask<1>(s, hlf, [&](int kk) { return sOff[kbase + kk] != OOB; });
+    }
+    bf16x8 pf[1][NKS];
+    if (w.template softmax<1>(s, pf, c)) w.rescale_o();
+    w.template pv<NKS>(pf, [&](int ks, int db) {
+      const char* a = vcur + v_lane + 16 * ks * VS + 64 * db;
+      return v_frag_tr(a, a + 8 * VS);
+    });
+    next = ahead;
+    // K(t+1) and V(t+1) have landed; K(t+2) may still be in flight
+    wait_vmcnt<RPW>();
+    barrier();
+  };
+
+  if (n_tiles > 0) {
+    const Offs o0 = offsets(0);
+    issue(rk, o0, sK0, KS);
+    issue(rv, o0, sV0, VS);
+    next = offsets(1);
+    issue(rk, next, sK1, KS);
+    wait_vmcnt<RPW>();  // K(0) and V(0) have landed
+    barrier();
+    for (int t = 0; t < n_tiles; t += 2) {
+      step(t, sK0, sV0, sV1);
+      if (t + 1 < n_tiles) step(t + 1, sK1, sV1, sV0);
+    }
+  }
+  // every DMA (also the zero-filling ones past the end) has landed and every
+  // wave is past its reads before the K stages are reused for the epilogue
+  wait_vmcnt<0>();
+  barrier();
+  constexpr int RB_BF16 = HDW * 2;
+  static_assert(2 * QW * RB_BF16 <= KT * KS, "epilogue staging");
+  if (is_bf16(p.out_mode)) {
+    char* const region = ((wave >> 1) == 0 ? sK0 : sK1) + dh * QW * RB_BF16;
+    w.store_lds(p, grow0, row0, split, lane, [&](int r) { return region + r * RB_BF16; }, col0,
+                dh == 0);
+    return;
+  }
+  w.store(p, grow0, row0, split, l32, hlf, col0, dh == 0);
+}
+
+}  // namespace
+
+int gather512_max_keys() { return G5_MAX_KEYS; }
+
+hipError_t launch_gather512(const FwdParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)p.tiles_per_group * p.n_groups * p.num_splits));
+  hipLaunchKernelGGL(fwd_gather512_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace fmha

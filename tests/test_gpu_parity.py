@@ -116,7 +116,7 @@ def test_split_with_empty_trailing_chunks(F):
     _case(F, w)
 
 
-@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
 @pytest.mark.parametrize("n_h", [1, 16, 128, 200])
 def test_gather(F, hd, n_h):
     w = W.make_custom(B=2, T=5, n_h=n_h, hd=hd, s_k=333, pool=4096, out_dtype="bf16",
@@ -124,12 +124,14 @@ def test_gather(F, hd, n_h):
     _case(F, w)
 
 
+@pytest.mark.parametrize("hd", [128, 512])
 @pytest.mark.parametrize("s_k,splits", [(1024, 1), (1025, 1), (1500, 1), (1500, 2)])
-def test_gather_list_lengths_around_the_staged_limit(F, s_k, splits):
-    """A split of up to 1024 gathered keys runs the kernel that stages its
-    index list in LDS; longer splits run the other gather kernel."""
-    w = W.make_custom(B=1, T=3, n_h=128, hd=128, s_k=s_k, pool=4096, out_dtype="bf16",
-                      num_splits=splits, seed=s_k + splits)
+def test_gather_list_lengths_around_the_staged_limit(F, hd, s_k, splits):
+    """A split of up to 1024 gathered keys runs a kernel that stages its
+    index list in LDS (hd 128 and 512); longer splits run the streaming
+    kernel's gather form."""
+    w = W.make_custom(B=1, T=3, n_h=128, hd=hd, s_k=s_k, pool=4096, out_dtype="bf16",
+                      num_splits=splits, seed=s_k + splits + hd)
     _case(F, w)
 
 
@@ -149,10 +151,11 @@ def test_gather_sorted_and_shuffled_indices_agree(F):
     assert (o1 - o2).abs().max().item() < 1e-3
 
 
-def test_gather_out_of_range_indices_are_masked(F):
+@pytest.mark.parametrize("hd", [128, 512])
+def test_gather_out_of_range_indices_are_masked(F, hd):
     """Entries outside [0, pool_rows) are never read and contribute nothing: the
     result equals attention over the valid entries only."""
-    w = W.make_custom(B=1, T=3, n_h=32, hd=128, s_k=200, pool=1000, out_dtype="f32", seed=17)
+    w = W.make_custom(B=1, T=3, n_h=32, hd=hd, s_k=200, pool=1000, out_dtype="f32", seed=17)
     q, k, v, idx = W.make_inputs(w)
     bad = idx.clone()
     bad[0, 0, 5] = -1
@@ -167,12 +170,13 @@ def test_gather_out_of_range_indices_are_masked(F):
     assert torch.all(out[0, 2] == 0) and torch.all(torch.isneginf(lse[0, 2]))
 
 
+@pytest.mark.parametrize("hd", [128, 512])
 @pytest.mark.parametrize("splits", [1, 3])
-def test_gather_repeated_indices_count_each_time(F, splits):
+def test_gather_repeated_indices_count_each_time(F, splits, hd):
     """A pool row listed several times is several keys (each takes its own
     softmax weight), as in the oracle's definition; a list of one repeated
     row gives that row's V exactly."""
-    w = W.make_custom(B=1, T=3, n_h=64, hd=128, s_k=256, pool=512, out_dtype="f32", seed=23)
+    w = W.make_custom(B=1, T=3, n_h=64, hd=hd, s_k=256, pool=512, out_dtype="f32", seed=23)
     q, k, v, idx = W.make_inputs(w)
     rep = idx.clone()
     rep[0, 0, 128:] = rep[0, 0, :128]        # every row twice
@@ -185,7 +189,7 @@ def test_gather_repeated_indices_count_each_time(F, splits):
 
 
 @pytest.mark.parametrize("hd,gather", [(64, False), (128, False), (256, False), (512, False),
-                                       (128, True), (256, True)])
+                                       (128, True), (256, True), (512, True)])
 def test_bf16_output_is_the_fp32_output_rounded_to_nearest_even(F, hd, gather):
     """The bf16 epilogue rounds the same fp32 values the fp32 epilogue stores,
     to nearest-even (torch's fp32 -> bf16 conversion is round-to-nearest-even)."""
