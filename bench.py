@@ -42,7 +42,7 @@ FLUSH_BYTES = 512 << 20
 # source makes those counters stale and the traffic field null.
 KERNEL_SOURCES = ["fmha_mqa_fwd_amd/csrc/fmha_fwd.hip", "fmha_mqa_fwd_amd/csrc/fmha_chunk.hip",
                   "fmha_mqa_fwd_amd/csrc/lse_merge.hip", "fmha_mqa_fwd_amd/csrc/fmha_device.h",
-                  "fmha_mqa_fwd_amd/csrc/fmha_gather512.hip"]
+                  "fmha_mqa_fwd_amd/csrc/fmha_hd512.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # which attention kernels (by demangled name) serve each workload
 WORKLOAD_KERNEL_SIG = {

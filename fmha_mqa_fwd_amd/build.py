@@ -24,7 +24,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libfmha_mqa.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["api.hip", "fmha_fwd.hip", "fmha_chunk.hip", "lse_merge.hip", "fmha_indexer.hip",
-           "gather_floor.hip", "fmha_gather512.hip"]
+           "gather_floor.hip", "fmha_hd512.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are kept out of the generated code on purpose; the
@@ -43,7 +43,7 @@ COMMON_FLAGS = [
 # it out and back on every tile for the (rare) rescale's multiplies; the
 # other kernels of these files compile to the same code either way.
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-SOURCE_FLAGS = {"fmha_gather512.hip": _VGPR_FORM, "fmha_fwd.hip": _VGPR_FORM,
+SOURCE_FLAGS = {"fmha_hd512.hip": _VGPR_FORM, "fmha_fwd.hip": _VGPR_FORM,
                 "fmha_chunk.hip": _VGPR_FORM}
 
 

@@ -559,8 +559,8 @@ hipError_t launch_fwd(FwdParams p, int hd, hipStream_t stream) {
       return gather ? launch_t<256, 32, 32, 4, 1, true>(p, stream)
                     : launch_t<256, 32, 32, 4, 1, false>(p, stream);
     case 512:
-      return gather ? (p.chunk <= gather512_max_keys() ? launch_gather512(p, stream)
-                                                       : launch_t<512, 32, 32, 4, 1, true>(p, stream))
+      if (p.chunk <= fwd512_max_keys()) return launch_fwd512(p, stream);
+      return gather ? launch_t<512, 32, 32, 4, 1, true>(p, stream)
                     : launch_t<512, 32, 32, 4, 1, false>(p, stream);
     default:
       return hipErrorInvalidValue;

@@ -1,11 +1,12 @@
-// Multi-query attention forward with the top-k row gather at head dim 512,
-// for gfx950.
+// Multi-query attention forward at head dim 512 for gfx950: the top-k row
+// gather, and dense keys (decode splits, a sliding window).
 //
 // The shape is DeepSeek-V4's (page "May 24, 2026 — Session Start Plan", Key
 // Numbers and File Map: head dim 512, Flash 64 query heads over top_k 512
 // gathered keys, Pro 128 heads over top_k 1024): every query head of a token
 // attends to the same s_k pool rows, picked by kv_idx (dsv4/kernels/cuda
-// commit log, KV row gather).
+// commit log, KV row gather); dense, every row of a batch attends to its
+// s_k keys.
 //
 // Work split, as in the streaming kernel's head-dim-512 form: four waves = two
 // blocks of 32 query rows x two halves of the head dim.  A wave holds its half
@@ -19,10 +20,11 @@
 //     offset is the row's pool offset + 16l, and the K and V instructions of a
 //     row share it.  The padding (K +16 bytes, V +64 bytes per row) keeps the
 //     operand reads free of bank conflicts with immediate offsets.
-//   * The split's index list is validated once and staged in LDS as pool byte
-//     offsets (OOB for an invalid entry or a key past the split: the row reads
-//     as zeros and its logit is masked).  A per-tile "has a masked key" bit
-//     lives in scalar registers.
+//   * The split's row offsets are staged in LDS once: gather, the index list
+//     validated into pool byte offsets; dense, the keys' offsets in the
+//     batch's K/V.  OOB marks an invalid entry or a key past the split (the
+//     row reads as zeros and its logit is masked).  A per-tile "has a masked
+//     key" bit lives in scalar registers.
 //   * Two K and two V stages.  K(t+2) is issued as soon as every wave is past
 //     QK^T(t) (the barrier of the S exchange), V(t+1) at the start of tile t;
 //     each tile ends with a wait that leaves K(t+2) in flight.  The DMA is
@@ -35,10 +37,11 @@ namespace {
 using namespace dev;
 
 constexpr int G5_HD = 512;
-constexpr int G5_MAX_KEYS = 1024;  // a split's index list held in LDS
+constexpr int G5_MAX_KEYS = 1024;  // a split's row offsets held in LDS
 
+template <bool GATHER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fwd_gather512_kernel(FwdParams p) {
+void fwd512_kernel(FwdParams p) {
   constexpr int HD = G5_HD, HDW = HD / 2, QW = 32, KT = 32, WAVES = 4, NKS = KT / 16;
   constexpr int M_WG = 2 * QW;              // two row blocks
   constexpr int ROW = HD * 2;               // bytes per K/V row
@@ -72,17 +75,27 @@ void fwd_gather512_kernel(FwdParams p) {
   const int n_tiles = (nk + KT - 1) / KT;
   const int row0 = tile * M_WG + (wave >> 1) * QW;
   const int64_t grow0 = (int64_t)group * p.rows_per_group;
-  const int32_t* ibase = p.kv_idx + (int64_t)group * p.s_k + key_lo;
 
-  const u32x4 rk = buffer_rsrc(p.k, (uint32_t)p.pool_rows * ROW);
-  const u32x4 rv = buffer_rsrc(p.v, (uint32_t)p.pool_rows * ROW);
+  // gather: the pools; dense: this batch's keys (byte counts fit 32 bits: the
+  // host checks rows * hd * 2)
+  const int64_t kv0 = GATHER ? 0 : (int64_t)group * p.s_k * HD;
+  const uint32_t kv_bytes = (uint32_t)(GATHER ? p.pool_rows : p.s_k) * ROW;
+  const u32x4 rk = buffer_rsrc(p.k + kv0, kv_bytes);
+  const u32x4 rv = buffer_rsrc(p.v + kv0, kv_bytes);
   const uint32_t lane16 = 16u * (uint32_t)lane;
 
-  // the split's index list, validated, as pool byte offsets
-  for (int i = tid; i < n_tiles * KT; i += 256) {
-    int idx = -1;
-    if (i < nk) idx = ibase[i];
-    sOff[i] = (idx >= 0 && idx < p.pool_rows) ? (uint32_t)idx * ROW : OOB;
+  // the split's row offsets: gather, the index list validated into pool byte
+  // offsets; dense, the keys' offsets in this batch's K/V
+  if constexpr (GATHER) {
+    const int32_t* ibase = p.kv_idx + (int64_t)group * p.s_k + key_lo;
+    for (int i = tid; i < n_tiles * KT; i += 256) {
+      int idx = -1;
+      if (i < nk) idx = ibase[i];
+      sOff[i] = (idx >= 0 && idx < p.pool_rows) ? (uint32_t)idx * ROW : OOB;
+    }
+  } else {
+    for (int i = tid; i < n_tiles * KT; i += 256)
+      sOff[i] = i < nk ? (uint32_t)(key_lo + i) * ROW : OOB;
   }
   Rows<HDW, QW, HD> w;
   w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf, col0);
@@ -209,11 +222,14 @@ void fwd_gather512_kernel(FwdParams p) {
 
 }  // namespace
 
-int gather512_max_keys() { return G5_MAX_KEYS; }
+int fwd512_max_keys() { return G5_MAX_KEYS; }
 
-hipError_t launch_gather512(const FwdParams& p, hipStream_t stream) {
+hipError_t launch_fwd512(const FwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles_per_group * p.n_groups * p.num_splits));
-  hipLaunchKernelGGL(fwd_gather512_kernel, grid, dim3(256), 0, stream, p);
+  if (p.kv_idx != nullptr)
+    hipLaunchKernelGGL(fwd512_kernel<true>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(fwd512_kernel<false>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -56,10 +56,10 @@ int64_t fwd_grid_size(const FwdParams& p, int hd);
 int chunk_max_keys(int hd);
 hipError_t launch_chunk(FwdParams p, int hd, hipStream_t stream);
 
-// fmha_gather512.hip: the top-k row gather at head dim 512 for splits of at
-// most gather512_max_keys() keys (p.tiles_per_group set for 64-row tiles).
-int gather512_max_keys();
-hipError_t launch_gather512(const FwdParams& p, hipStream_t stream);
+// fmha_hd512.hip: head dim 512, gather or dense, for splits of at most
+// fwd512_max_keys() keys (p.tiles_per_group set for 64-row tiles).
+int fwd512_max_keys();
+hipError_t launch_fwd512(const FwdParams& p, hipStream_t stream);
 
 // out[r] = sum_i w_i o_i[r] / sum_i w_i with w_i = exp(lse_i[r] - max_i lse_i[r]).
 // o_parts holds fp32, or bf16 when parts_bf16.  With sink (optional,

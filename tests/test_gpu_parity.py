@@ -353,6 +353,15 @@ def test_hd512_flash_topk_benchmarked_size_sampled(F):
     _case(F, w, rows=_sample_rows(w.rows, 254, 8))
 
 
+@pytest.mark.parametrize("s_k,splits", [(1024, 1), (1025, 1), (2000, 1), (2000, 2)])
+def test_hd512_dense_key_counts_around_the_staged_limit(F, s_k, splits):
+    """At head dim 512 a split of up to 1024 keys runs the kernel that stages
+    its row offsets in LDS; longer splits run the streaming kernel."""
+    w = W.make_custom(B=2, T=3, n_h=24, hd=512, s_k=s_k, out_dtype="bf16", num_splits=splits,
+                      seed=s_k + 7 * splits)
+    _case(F, w)
+
+
 @pytest.mark.parametrize("splits,out_dtype", [(1, "f32"), (3, "f32"), (2, "bf16")])
 def test_hd512_dense_prefill(F, splits, out_dtype):
     w = W.make_custom(B=1, T=40, n_h=8, hd=512, s_k=700, out_dtype=out_dtype, num_splits=splits,
