@@ -510,8 +510,8 @@ def cpu_baseline(budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=[n for n, _ in CASES] + ["all"],
                     help="profile mode: run one workload back to back, no JSON line")
@@ -646,6 +646,8 @@ def main():
         "decode": {"value": round(d["gbps"], 1), "unit": "GB/s",
                    "frac_of_hbm_peak": round(d["gbps"] / PEAK_HBM_GBPS, 4),
                    "us_per_call": round(d["ms"] * 1e3, 2),
+                   "us_median": round(d["ms_median"] * 1e3, 2),
+                   "us_p10": round(d["ms_p10"] * 1e3, 2), "us_p90": round(d["ms_p90"] * 1e3, 2),
                    "us_per_call_warm": round(d["ms_warm"] * 1e3, 2),
                    "algorithmic_bytes": d["bytes"], "workload": d["workload"],
                    "hbm_copy_GBps": round(copy_gbps, 1),
@@ -657,6 +659,8 @@ def main():
                         "gather_floor_us_warm": round(s["floor_ms_warm"] * 1e3, 2),
                         "gather_floor_GBps": round(s["floor_gbps"], 1),
                         "us_per_call": round(s["ms"] * 1e3, 2),
+                        "us_median": round(s["ms_median"] * 1e3, 2),
+                        "us_p10": round(s["ms_p10"] * 1e3, 2), "us_p90": round(s["ms_p90"] * 1e3, 2),
                         "us_per_call_warm": round(s["ms_warm"] * 1e3, 2),
                         "workload": s["workload"]},
         "prefill_detail": {"us_per_call": round(p["ms"] * 1e3, 2),
