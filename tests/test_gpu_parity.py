@@ -103,16 +103,18 @@ def test_ragged_row_counts(F, hd, rows):
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 8, 13])
-@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
 def test_split_kv(F, splits, hd):
     w = W.make_custom(B=3, T=1, n_h=128, hd=hd, s_k=1000, out_dtype="bf16",
                       num_splits=splits, seed=splits * 31 + hd)
     _case(F, w)
 
 
-def test_split_with_empty_trailing_chunks(F):
+@pytest.mark.parametrize("hd,pool", [(128, 0), (512, 0), (128, 300), (512, 300)])
+def test_split_with_empty_trailing_chunks(F, hd, pool):
     # 9 keys in 8 chunks of 2: chunks 5..7 are empty (lse -inf) and must vanish
-    w = W.make_custom(B=2, T=1, n_h=16, hd=128, s_k=9, out_dtype="f32", num_splits=8, seed=9)
+    w = W.make_custom(B=2, T=1, n_h=16, hd=hd, s_k=9, pool=pool, out_dtype="f32", num_splits=8,
+                      seed=9 + hd + pool)
     _case(F, w)
 
 
