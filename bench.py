@@ -48,7 +48,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 WORKLOAD_KERNEL_SIG = {
     "mqa_prefill": lambda k: "fwd_kernel<128" in k and ", false," in k,
     "mqa_decode": lambda k: "chunk_kernel" in k or "merge_kernel" in k,
-    "sparse_topk": lambda k: "fwd_gather_sw_kernel<128" in k,
+    "sparse_topk": lambda k: "fwd_gather_staged_kernel<128" in k,
 }
 
 

@@ -320,34 +320,41 @@ void fwd_kernel(FwdParams p) {
 }
 
 // ------------------------------------------------------------------------
-// Gather kernel with a three-stage pipeline on unpadded, XOR-swizzled K/V
-// stages (16-byte chunk c of row r stored at chunk c ^ swz(r), so the operand
-// reads stay free of bank conflicts without pad bytes): a 32-key stage is
-// 32 x hd x 2 bytes per tensor.  Two workgroups share a CU (three would
-// spill registers: the swizzled operand addresses do not fold into immediate
-// offsets), each with two tiles in flight.  The DMA of tile t+2 streams while tile t is
-// computed; each tile ends with a wait that leaves only that newest DMA
-// outstanding, then a plain s_barrier.  The split's index list (validated)
-// is staged in LDS first, so the loop issues no global loads; the DMA is
-// issued from inline assembly so the compiler adds no waits of its own.
+// Gather kernel for splits of at most GSW_MAX_KEYS keys (hd 64/128/256).
+// Same tile shape, padded LDS rows and operand reads as fwd_kernel; what
+// differs is how the gathered rows are moved:
+//   * the split's index list is validated once and staged in LDS as pool
+//     byte offsets (OOB for an invalid entry or a key past the split), and a
+//     per-tile "has a masked key" bit is kept in scalar registers, so the
+//     loop issues no global loads and tests no index per key;
+//   * the per-lane DMA offsets of tile t+1 are read from that list one tile
+//     ahead (during tile t-1), so no DMA waits on an LDS read;
+//   * every wave issues the same number of DMA instructions per tile (slots
+//     past a tile's last instruction write zeros to a spare KiB of LDS), and
+//     the DMA is issued from inline assembly with one explicit vmcnt wait per
+//     tile, so the compiler adds no waits of its own.
+// Without a swizzle the operand addresses are a base register plus immediate
+// offsets, which keeps the hd 128 kernel within 168 VGPRs: three workgroups
+// per CU.
 constexpr int GSW_MAX_KEYS = 1024;  // a split's index list held in LDS
 
 template <int HD, int WPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void fwd_gather_sw_kernel(FwdParams p) {
-  constexpr int WAVES = 4, QW = 32, KT = 32, NKB = 1, NKS = 2;
+void fwd_gather_staged_kernel(FwdParams p) {
+  constexpr int WAVES = 4, QW = 32, KT = 32, NKB = 1, NKS = KT / 16;
   constexpr int M_WG = WAVES * QW;
-  constexpr int ROW = HD * 2;                  // bytes per row (unpadded)
-  constexpr int CPR = ROW / 16;                // 16-byte chunks per row
-  constexpr int STAGE = KT * ROW;              // bytes per tensor per stage
-  constexpr int NI = STAGE / 1024;             // DMA instructions per tensor per tile
-  static_assert(NI % WAVES == 0, "every wave issues the same DMA count");
-  constexpr int J = NI / WAVES;                // per wave per tensor
-  constexpr int PER_TILE = 2 * J;              // this wave's DMAs per tile (K and V)
+  constexpr int ROW = Lds<HD>::ROW;
+  constexpr int KS = Lds<HD>::K_STRIDE;
+  constexpr int VS = Lds<HD>::V_STRIDE;
+  constexpr int NKI = (KT * KS + 1023) / 1024;   // DMA instructions per K tile
+  constexpr int NVI = (KT * VS + 1023) / 1024;   // ... per V tile
+  constexpr int KJ = (NKI + WAVES - 1) / WAVES;  // per wave (slots past NKI: the spare KiB)
+  constexpr int VJ = (NVI + WAVES - 1) / WAVES;
 
-  __shared__ __attribute__((aligned(1024))) char sK0[STAGE], sK1[STAGE], sK2[STAGE];
-  __shared__ __attribute__((aligned(1024))) char sV0[STAGE], sV1[STAGE], sV2[STAGE];
-  __shared__ int sIdx[GSW_MAX_KEYS];
+  __shared__ __attribute__((aligned(1024))) char sK0[NKI * 1024], sK1[NKI * 1024];
+  __shared__ __attribute__((aligned(1024))) char sV0[NVI * 1024], sV1[NVI * 1024];
+  __shared__ __attribute__((aligned(1024))) char sSpare[1024];
+  __shared__ uint32_t sOff[GSW_MAX_KEYS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -369,44 +376,53 @@ void fwd_gather_sw_kernel(FwdParams p) {
   const int64_t grow0 = (int64_t)group * p.rows_per_group;
   const int32_t* ibase = p.kv_idx + (int64_t)group * p.s_k + key_lo;
 
-  // DMA geometry: instruction j of this wave fills stage bytes
-  // [1024 (wave + 4 j), +1024): lane -> (row, physical chunk)
-  int drow[J], dphys[J];
+  // DMA geometry (as fwd_kernel): slot j of this wave is instruction
+  // wave + 4j, whose lane `lane` fills tile bytes [1024 inst + 16 lane, +16):
+  // row r (-1: pad bytes, past the tile, or a spare slot) and column byte c
+  int kr[KJ], kc[KJ], vr[VJ], vc[VJ];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int pos = (wave + WAVES * j) * 1024 + lane * 16;
-    drow[j] = pos / ROW;
-    dphys[j] = (pos % ROW) / 16;
+  for (int j = 0; j < KJ; ++j) {
+    const int inst = wave + WAVES * j;
+    const int pos = inst * 1024 + lane * 16;
+    const int r = pos / KS, cc = pos % KS;
+    kr[j] = (inst < NKI && cc < ROW && r < KT) ? r : -1;
+    kc[j] = cc;
+  }
+#pragma unroll
+  for (int j = 0; j < VJ; ++j) {
+    const int inst = wave + WAVES * j;
+    const int pos = inst * 1024 + lane * 16;
+    const int r = pos / VS, cc = pos % VS;
+    vr[j] = (inst < NVI && cc < ROW && r < KT) ? r : -1;
+    vc[j] = cc;
   }
   const u32x4 rk = buffer_rsrc(p.k, (uint32_t)p.pool_rows * ROW);
   const u32x4 rv = buffer_rsrc(p.v, (uint32_t)p.pool_rows * ROW);
   struct Offs {
-    uint32_t k[J], v[J];
+    uint32_t k[KJ], v[VJ];
   };
-  // byte offsets of this lane's DMA chunks for tile t (OOB: masked key or past the end)
+  // this lane's DMA offsets for tile t (OOB + column stays out of range)
   auto offsets = [&](int t) __attribute__((always_inline)) {
     Offs o;
     const bool live = t < n_tiles;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      o.k[j] = OOB;
-      o.v[j] = OOB;
-      if (live) {
-        const int idx = sIdx[t * KT + drow[j]];
-        if (idx >= 0) {
-          o.k[j] = (uint32_t)idx * ROW + 16u * (dphys[j] ^ swz_k<CPR>(drow[j]));
-          o.v[j] = (uint32_t)idx * ROW + 16u * (dphys[j] ^ swz_v<CPR>(drow[j]));
-        }
-      }
-    }
+    for (int j = 0; j < KJ; ++j)
+      o.k[j] = (live && kr[j] >= 0) ? sOff[t * KT + kr[j]] + (uint32_t)kc[j] : OOB;
+#pragma unroll
+    for (int j = 0; j < VJ; ++j)
+      o.v[j] = (live && vr[j] >= 0) ? sOff[t * KT + vr[j]] + (uint32_t)vc[j] : OOB;
     return o;
   };
   auto issue = [&](const Offs& o, char* kbuf, char* vbuf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
+    for (int j = 0; j < KJ; ++j) {
       const int inst = wave + WAVES * j;
-      dma16(rk, (uint32_t)(uintptr_t)(kbuf + inst * 1024), o.k[j]);
-      dma16(rv, (uint32_t)(uintptr_t)(vbuf + inst * 1024), o.v[j]);
+      dma16(rk, (uint32_t)(uintptr_t)(inst < NKI ? kbuf + inst * 1024 : sSpare), o.k[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < VJ; ++j) {
+      const int inst = wave + WAVES * j;
+      dma16(rv, (uint32_t)(uintptr_t)(inst < NVI ? vbuf + inst * 1024 : sSpare), o.v[j]);
     }
   };
   auto barrier = [&]() __attribute__((always_inline)) {
@@ -420,73 +436,67 @@ void fwd_gather_sw_kernel(FwdParams p) {
   const float c = p.scale_log2;
   const int jj = lane & 15;
   const int dsub = (lane >> 4) & 1;
-  const int kx = swz_k<CPR>(l32);  // K operand row l32
-  Offs ahead;
+  // per-lane operand offsets within a tile buffer (see fwd_kernel)
+  const int k_lane = l32 * KS + 16 * hlf;
+  const int v_lane = (4 * hlf + (jj >> 2)) * VS + 2 * (16 * dsub + 4 * (jj & 3));
+  Offs ahead;                // offsets of tile t+1, read during tile t-1
   uint64_t tile_masked = 0;  // bit t: tile t has a masked key
 
-  auto step = [&](int t, const char* kcur, const char* vcur, char* kfar, char* vfar)
+  auto step = [&](int t, const char* kcur, const char* vcur, char* knext, char* vnext)
       __attribute__((always_inline)) {
-    issue(ahead, kfar, vfar);  // tile t+2
-    ahead = offsets(t + 3);
+    issue(ahead, knext, vnext);  // tile t+1
+    ahead = offsets(t + 2);
     f32x16 s[NKB][1];
     w.template qk<NKB>(s, [&](int, int ds) {
-      return *reinterpret_cast<const bf16x8*>(kcur + l32 * ROW + 16 * ((2 * ds + hlf) ^ kx));
+      return *reinterpret_cast<const bf16x8*>(kcur + k_lane + ds * 32);
     });
-    const int kbase = t * KT;
     if ((tile_masked >> t) & 1) {
-      w.template mask<NKB>(s, hlf, [&](int kk) { return sIdx[kbase + kk] >= 0; });
+      const int kbase = t * KT;
+      w.template mask<NKB>(s, hlf, [&](int kk) { return sOff[kbase + kk] != OOB; });
     }
     bf16x8 pf[1][NKS];
     if (w.template softmax<NKB>(s, pf, c)) w.rescale_o();
     w.template pv<NKS>(pf, [&](int ks, int db) {
-      const int r0 = 16 * ks + 4 * hlf + (jj >> 2);
-      const int r1 = r0 + 8;
-      const int ch = 4 * db + 2 * dsub + ((jj & 3) >> 1);
-      const int sub = 8 * (jj & 1);
-      return v_frag_tr(vcur + r0 * ROW + 16 * (ch ^ swz_v<CPR>(r0)) + sub,
-                       vcur + r1 * ROW + 16 * (ch ^ swz_v<CPR>(r1)) + sub);
+      const char* a = vcur + v_lane + 16 * ks * VS + 64 * db;
+      return v_frag_tr(a, a + 8 * VS);
     });
-    // tile t+1 (issued a step ago) has landed; tile t+2 may still be in flight
-    wait_vmcnt<PER_TILE>();
+    wait_vmcnt<0>();  // tile t+1 has landed
     barrier();
   };
 
-  // the split's index list, validated, in LDS (keys past the split: masked)
+  // the split's index list, validated, as pool byte offsets
   for (int i = tid; i < n_tiles * KT; i += 256) {
     int idx = -1;
     if (i < nk) idx = ibase[i];
-    sIdx[i] = (idx >= 0 && idx < p.pool_rows) ? idx : -1;
+    sOff[i] = (idx >= 0 && idx < p.pool_rows) ? (uint32_t)idx * ROW : OOB;
   }
-  // Q and the index list are in before any DMA is issued, so the compiler's
-  // own waits for them stay out of the loop
+  // Q and the list are in before any DMA is issued, so the compiler's own
+  // waits for them stay out of the loop
   wait_vmcnt<0>();
   __syncthreads();
   for (int r = 0; r < n_tiles; r += 2) {  // each wave reads the list two tiles at a time
     const int i = r * KT + lane;
-    const uint64_t b = __ballot(i < n_tiles * KT && sIdx[min(i, GSW_MAX_KEYS - 1)] < 0);
+    const uint64_t b = __ballot(i < n_tiles * KT && sOff[min(i, GSW_MAX_KEYS - 1)] == OOB);
     tile_masked |= (((uint32_t)b != 0) ? 1ull : 0ull) << r;
     tile_masked |= (((uint32_t)(b >> 32) != 0) ? 1ull : 0ull) << (r + 1);
   }
   if (n_tiles > 0) {
     issue(offsets(0), sK0, sV0);
-    issue(offsets(1), sK1, sV1);
-    ahead = offsets(2);
-    wait_vmcnt<PER_TILE>();  // tile 0 has landed
+    ahead = offsets(1);
+    wait_vmcnt<0>();  // tile 0 has landed
     barrier();
-    for (int t = 0; t < n_tiles; t += 3) {
-      step(t, sK0, sV0, sK2, sV2);
+    for (int t = 0; t < n_tiles; t += 2) {
+      step(t, sK0, sV0, sK1, sV1);
       if (t + 1 < n_tiles) step(t + 1, sK1, sV1, sK0, sV0);
-      if (t + 2 < n_tiles) step(t + 2, sK2, sV2, sK1, sV1);
     }
   }
-  // every DMA (also the zero-filling ones past the end) has landed and every
-  // wave is past its reads before the stages are reused for the epilogue
+  // every wave is past its reads before the buffers are reused for the epilogue
   wait_vmcnt<0>();
   barrier();
   constexpr int RB_BF16 = HD * 2;
-  if constexpr (QW * RB_BF16 <= STAGE) {
+  if constexpr (QW * RB_BF16 <= NKI * 1024) {
     if (is_bf16(p.out_mode)) {
-      char* const region = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sK2 : sV0;
+      char* const region = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1;
       w.store_lds(p, grow0, row0, split, lane, [&](int r) { return region + r * RB_BF16; });
       return;
     }
@@ -495,9 +505,9 @@ void fwd_gather_sw_kernel(FwdParams p) {
 }
 
 template <int HD, int WPE>
-hipError_t launch_gather_sw(const FwdParams& p, hipStream_t stream) {
+hipError_t launch_gather_staged(const FwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles_per_group * p.n_groups * p.num_splits));
-  hipLaunchKernelGGL((fwd_gather_sw_kernel<HD, WPE>), grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fwd_gather_staged_kernel<HD, WPE>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -506,10 +516,13 @@ struct Shape {
   int rows() const { return waves * qw; }  // rows per workgroup (before a head-dim split)
 };
 
-// 32 rows per wave keeps a wave within 170 (dense, 32-key tiles: three waves
-// per SIMD) or 256 (gather, 64-key tiles: two waves per SIMD) registers, so
-// one wave's softmax overlaps other waves' MFMAs.  hd 256 needs the whole
-// register file: one wave per SIMD.
+// Rows per workgroup of each kernel (fwd_kernel for dense keys and for
+// gather splits of more than GSW_MAX_KEYS keys, fwd_gather_staged_kernel
+// otherwise): 4 waves x 32 rows, or 2 row blocks of 32 at hd 512.  32 rows per
+// wave keeps a wave within 170 registers (dense hd <= 128 and the staged
+// gather at hd 128: three waves per SIMD) or 256 (the long-split gather form,
+// 64-key tiles: two waves per SIMD), so one wave's softmax overlaps other
+// waves' MFMAs.  hd 256 needs the whole register file: one wave per SIMD.
 Shape pick_shape(int hd, bool gather) {
   if (hd > 256) return {32, 32, 2, 1};  // 2 row blocks x 2 head-dim halves = 4 waves
   if (hd >= 256) return {32, 32, 4, 1};
@@ -549,14 +562,16 @@ hipError_t launch_fwd(FwdParams p, int hd, hipStream_t stream) {
   p.tiles_per_group = (p.rows_per_group + m_wg - 1) / m_wg;
   switch (hd) {
     case 64:
-      return gather ? launch_t<64, 32, 64, 4, 2, true>(p, stream)
+      return gather ? (p.chunk <= GSW_MAX_KEYS ? launch_gather_staged<64, 4>(p, stream)
+                                               : launch_t<64, 32, 64, 4, 2, true>(p, stream))
                     : launch_t<64, 32, 32, 4, 3, false>(p, stream);
     case 128:
-      return gather ? (p.chunk <= GSW_MAX_KEYS ? launch_gather_sw<128, 2>(p, stream)
+      return gather ? (p.chunk <= GSW_MAX_KEYS ? launch_gather_staged<128, 3>(p, stream)
                                                : launch_t<128, 32, 64, 4, 2, true>(p, stream))
                     : launch_t<128, 32, 32, 4, 3, false>(p, stream);
     case 256:
-      return gather ? launch_t<256, 32, 32, 4, 1, true>(p, stream)
+      return gather ? (p.chunk <= GSW_MAX_KEYS ? launch_gather_staged<256, 1>(p, stream)
+                                               : launch_t<256, 32, 32, 4, 1, true>(p, stream))
                     : launch_t<256, 32, 32, 4, 1, false>(p, stream);
     case 512:
       if (p.chunk <= fwd512_max_keys()) return launch_fwd512(p, stream);

@@ -126,12 +126,11 @@ def test_gather(F, hd, n_h):
     _case(F, w)
 
 
-@pytest.mark.parametrize("hd", [128, 512])
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
 @pytest.mark.parametrize("s_k,splits", [(1024, 1), (1025, 1), (1500, 1), (1500, 2)])
 def test_gather_list_lengths_around_the_staged_limit(F, hd, s_k, splits):
     """A split of up to 1024 gathered keys runs a kernel that stages its
-    index list in LDS (hd 128 and 512); longer splits run the streaming
-    kernel's gather form."""
+    index list in LDS; longer splits run the streaming kernel's gather form."""
     w = W.make_custom(B=1, T=3, n_h=128, hd=hd, s_k=s_k, pool=4096, out_dtype="bf16",
                       num_splits=splits, seed=s_k + splits + hd)
     _case(F, w)
@@ -153,7 +152,7 @@ def test_gather_sorted_and_shuffled_indices_agree(F):
     assert (o1 - o2).abs().max().item() < 1e-3
 
 
-@pytest.mark.parametrize("hd", [128, 512])
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
 def test_gather_out_of_range_indices_are_masked(F, hd):
     """Entries outside [0, pool_rows) are never read and contribute nothing: the
     result equals attention over the valid entries only."""
@@ -172,7 +171,7 @@ def test_gather_out_of_range_indices_are_masked(F, hd):
     assert torch.all(out[0, 2] == 0) and torch.all(torch.isneginf(lse[0, 2]))
 
 
-@pytest.mark.parametrize("hd", [128, 512])
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
 @pytest.mark.parametrize("splits", [1, 3])
 def test_gather_repeated_indices_count_each_time(F, splits, hd):
     """A pool row listed several times is several keys (each takes its own
