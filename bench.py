@@ -148,8 +148,9 @@ class FloorCase:
 class SourcesCase:
     """Decode over two key sources — top-k rows gathered from a compressed
     pool plus a dense sliding window — in one softmax: one forward per source
-    into fp32 partials, then the LSE merge (the composition fwd_sources runs),
-    with every launch's arguments marshalled once."""
+    writes its split partials (fmha_mqa_fwd_partials) into planes of one fp32
+    buffer, then one LSE merge over all planes (the composition fwd_sources
+    runs), with every launch's arguments marshalled once."""
 
     def __init__(self, dev, B=32, n_h=64, hd=512, top_k=512, pool=32768, window=128,
                  splits=(8, 4)):
@@ -164,20 +165,22 @@ class SourcesCase:
         self.q, kp, vp, idx, kw, vw = (t.to(dev) for t in (q, kp, vp, idx, kw, vw))
         self._keep = (kp, vp, idx, kw, vw)
         rows = B * n_h
-        self.parts = torch.empty((2, B, 1, n_h, hd), dtype=torch.float32, device=dev)
-        self.lse_parts = torch.empty((2, B, 1, n_h), dtype=torch.float32, device=dev)
+        n_parts = splits[0] + splits[1]
+        self.parts = torch.empty((n_parts, B, 1, n_h, hd), dtype=torch.float32, device=dev)
+        self.lse_parts = torch.empty((n_parts, B, 1, n_h), dtype=torch.float32, device=dev)
         self.out = torch.empty((B, 1, n_h, hd), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, 1, n_h), dtype=torch.float32, device=dev)
         # one token per sequence leaves a source's rows few: split its keys so
-        # that each launch fills the chip (each split forward merges its own
-        # partials, then the two sources are merged)
-        self.plans = [F.FwdPlan(self.q, kp, vp, idx, scale=top.scale, out_dtype=torch.float32,
-                                num_splits=splits[0], out=self.parts[0], lse=self.lse_parts[0]),
-                      F.FwdPlan(self.q, kw, vw, None, scale=top.scale, out_dtype=torch.float32,
-                                num_splits=splits[1], out=self.parts[1], lse=self.lse_parts[1])]
+        # that each launch fills the chip; every split's partial goes to the
+        # one merge
+        s0 = splits[0]
+        self.plans = [F.FwdPlan(self.q, kp, vp, idx, scale=top.scale, num_splits=s0,
+                                out=self.parts[:s0], lse=self.lse_parts[:s0], partials=True),
+                      F.FwdPlan(self.q, kw, vw, None, scale=top.scale, num_splits=splits[1],
+                                out=self.parts[s0:], lse=self.lse_parts[s0:], partials=True)]
         lib = F._binding._lib
         self._merge = lib.fmha_lse_merge
-        self._margs = (self.parts.data_ptr(), self.lse_parts.data_ptr(), 2, rows, hd,
+        self._margs = (self.parts.data_ptr(), self.lse_parts.data_ptr(), n_parts, rows, hd,
                        self.out.data_ptr(), F.FMHA_BF16, self.lse.data_ptr(),
                        torch.cuda.current_stream().cuda_stream)
         # bytes the method must move once: Q, gathered top-k K/V rows (+ idx),

@@ -30,6 +30,9 @@ SIGNATURES = {
                                    _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_float, _c_int, _c_int, _c_void_p, _c_size, _c_void_p,
                                    _c_void_p]),
+    "fmha_mqa_fwd_partials": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                       _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_int, _c_float, _c_int, _c_void_p]),
     "fmha_attention_sink": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int,
                                      _c_int, _c_void_p]),
     "fmha_lse_merge": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
@@ -121,6 +124,10 @@ class FwdPlan:
     Calling the plan launches the forward again on the same tensors and
     stream (for loops and timing, where per-call Python work would otherwise
     sit between launches); it returns (out, lse).  Arguments as for `fwd`.
+    With partials=True the plan calls fmha_mqa_fwd_partials instead: out and
+    lse are then the fp32 split planes [num_splits, B, T, n_h, hd] and
+    [num_splits, B, T, n_h] (allocated when None); out_dtype, workspace and
+    sink do not apply.
     """
 
     def __init__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -128,7 +135,7 @@ class FwdPlan:
                  out_dtype: torch.dtype = torch.bfloat16, num_splits: int = 1,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None, stream=None,
-                 sink: Optional[torch.Tensor] = None):
+                 sink: Optional[torch.Tensor] = None, partials: bool = False):
         if q.dim() != 4:
             raise ValueError("q must be [B, T, n_h, hd]")
         B, T, n_h, hd = q.shape
@@ -154,6 +161,25 @@ class FwdPlan:
                 raise ValueError("sink must be a contiguous float32 [n_h] tensor")
         dev = q.device
         _same_gpu(dev, k=k, v=v, kv_idx=kv_idx, sink=sink, out=out, lse=lse, workspace=workspace)
+        if partials:
+            if sink is not None or workspace is not None:
+                raise ValueError("partials take neither a sink nor a workspace")
+            if scale is None:
+                scale = default_scale(hd)
+            S = int(num_splits)
+            if out is None:
+                out = torch.empty((S, B, T, n_h, hd), dtype=torch.float32, device=dev)
+            if lse is None:
+                lse = torch.empty((S, B, T, n_h), dtype=torch.float32, device=dev)
+            _check_buf("o_parts", out, (S, B, T, n_h, hd), (torch.float32,))
+            _check_buf("lse_parts", lse, (S, B, T, n_h), (torch.float32,))
+            self._keep = (q, k, v, kv_idx)
+            self.out, self.lse = out, lse
+            self._fn = _lib.fmha_mqa_fwd_partials
+            self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(out), _ptr(lse),
+                          B, T, n_h, s_k, hd, pool_rows, float(scale), S,
+                          _stream_handle(stream))
+            return
         if out is not None:
             _check_buf("out", out, (B, T, n_h, hd), (torch.float32, torch.bfloat16))
         if lse is not None:
@@ -205,6 +231,18 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    sink)()
 
 
+def fwd_partials(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 kv_idx: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                 num_splits: int = 1, o_parts: Optional[torch.Tensor] = None,
+                 lse_parts: Optional[torch.Tensor] = None, stream=None
+                 ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fmha_mqa_fwd_partials: the split-KV forward without its merge.  Returns
+    the fp32 planes (o_parts [num_splits, B, T, n_h, hd], lse_parts
+    [num_splits, B, T, n_h]); arguments as for `fwd`."""
+    return FwdPlan(q, k, v, kv_idx, scale, num_splits=num_splits, out=o_parts, lse=lse_parts,
+                   stream=stream, partials=True)()
+
+
 def fwd_sources(q: torch.Tensor, sources, scale: Optional[float] = None,
                 out_dtype: torch.dtype = torch.bfloat16, sink: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
@@ -214,9 +252,10 @@ def fwd_sources(q: torch.Tensor, sources, scale: Optional[float] = None,
 
     sources: sequence of (k, v, kv_idx, num_splits) — dense k, v [B, S, hd]
     with kv_idx None, or pools [P, hd] with kv_idx [B, T, S]; num_splits as
-    for fwd.  Each source runs through fmha_mqa_fwd into fp32 partials, which
-    fmha_lse_merge combines; the sink (fp32 [n_h]) joins once, after the
-    merge (fmha_attention_sink).  Returns (out [B, T, n_h, hd], lse [B, T, n_h]).
+    for fwd.  Each source writes its split partials with fmha_mqa_fwd_partials
+    into its own planes of one fp32 buffer, and one fmha_lse_merge combines
+    all planes; the sink (fp32 [n_h]) joins once, after the merge
+    (fmha_attention_sink).  Returns (out [B, T, n_h, hd], lse [B, T, n_h]).
     """
     if q.dim() != 4:
         raise ValueError("q must be [B, T, n_h, hd]")
@@ -231,18 +270,20 @@ def fwd_sources(q: torch.Tensor, sources, scale: Optional[float] = None,
     if lse is not None:
         _check_buf("lse", lse, (B, T, n_h), (torch.float32,))
     rows = B * T * n_h
-    parts = torch.empty((n, B, T, n_h, hd), dtype=torch.float32, device=dev)
-    lse_parts = torch.empty((n, B, T, n_h), dtype=torch.float32, device=dev)
-    for i, src in enumerate(sources):
-        k, v, kv_idx = src[0], src[1], src[2]
-        splits = src[3] if len(src) > 3 else 1
-        fwd(q, k, v, kv_idx, scale, torch.float32, splits, out=parts[i], lse=lse_parts[i],
-            stream=stream)
+    splits = [int(src[3]) if len(src) > 3 else 1 for src in sources]
+    total = sum(splits)
+    parts = torch.empty((total, B, T, n_h, hd), dtype=torch.float32, device=dev)
+    lse_parts = torch.empty((total, B, T, n_h), dtype=torch.float32, device=dev)
+    first = 0
+    for src, s in zip(sources, splits):
+        fwd_partials(q, src[0], src[1], src[2], scale, s, o_parts=parts[first:first + s],
+                     lse_parts=lse_parts[first:first + s], stream=stream)
+        first += s
     if out is None:
         out = torch.empty((B, T, n_h, hd), dtype=out_dtype, device=dev)
     if lse is None:
         lse = torch.empty((B, T, n_h), dtype=torch.float32, device=dev)
-    lse_merge(parts.view(n, rows, hd), lse_parts.view(n, rows), out.dtype,
+    lse_merge(parts.view(total, rows, hd), lse_parts.view(total, rows), out.dtype,
               out=out.view(rows, hd), lse=lse.view(rows), stream=stream)
     if sink is not None:
         apply_sink(out, lse, sink, stream=stream)

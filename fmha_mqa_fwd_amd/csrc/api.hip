@@ -36,11 +36,14 @@ inline WsLayout ws_layout(int64_t rows, int hd, int splits) {
 
 inline int launch_status(hipError_t e) { return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH; }
 
-// The forward of fmha_mqa_fwd / fmha_mqa_fwd_sink (sink: nullptr or [n_h]).
+// The forward of fmha_mqa_fwd / fmha_mqa_fwd_sink (sink: nullptr or [n_h]),
+// and, with partials_only, of fmha_mqa_fwd_partials: out/lse are then the
+// caller's fp32 partial planes [num_splits, rows, hd] / [num_splits, rows],
+// written without a merge (out_dtype, sink and workspace unused).
 int fwd_impl(const void* q, const void* k, const void* v, const int32_t* kv_idx, void* out,
              float* lse, int B, int T, int n_h, int s_k, int hd, int pool_rows, float scale,
              int out_dtype, int num_splits, void* workspace, size_t workspace_bytes,
-             void* stream, const float* sink) {
+             void* stream, const float* sink, bool partials_only = false) {
   if (out_dtype != FMHA_F32 && out_dtype != FMHA_BF16) return FMHA_ERR_INVALID_ARG;
   if (B < 0 || T < 0 || n_h < 0 || s_k < 0 || num_splits < 1) return FMHA_ERR_INVALID_ARG;
   if (hd != 64 && hd != 128 && hd != 256 && hd != 512) return FMHA_ERR_UNSUPPORTED;
@@ -87,6 +90,12 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* kv_idx,
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // launch errors below are ours alone
 
+  if (partials_only) {
+    p.out = out;
+    p.lse = lse;
+    p.out_mode = fmha::OUT_PARTIAL;
+    return launch_status(fmha::launch_fwd(p, hd, st));
+  }
   if (num_splits == 1) {
     p.out = out;
     p.lse = lse;
@@ -139,6 +148,13 @@ int fmha_mqa_fwd_sink(const void* q, const void* k, const void* v, const int32_t
   if (!sink) return FMHA_ERR_INVALID_ARG;
   return fwd_impl(q, k, v, kv_idx, out, lse, B, T, n_h, s_k, hd, pool_rows, scale, out_dtype,
                   num_splits, workspace, workspace_bytes, stream, sink);
+}
+
+int fmha_mqa_fwd_partials(const void* q, const void* k, const void* v, const int32_t* kv_idx,
+                          float* o_parts, float* lse_parts, int B, int T, int n_h, int s_k,
+                          int hd, int pool_rows, float scale, int num_splits, void* stream) {
+  return fwd_impl(q, k, v, kv_idx, o_parts, lse_parts, B, T, n_h, s_k, hd, pool_rows, scale,
+                  FMHA_F32, num_splits, nullptr, 0, stream, nullptr, true);
 }
 
 int fmha_attention_sink(void* out, float* lse, const float* sink, int rows, int n_h, int hd,

@@ -106,6 +106,22 @@ int fmha_mqa_fwd_sink(const void* q, const void* k, const void* v,
                       void* workspace, size_t workspace_bytes, void* stream,
                       const float* sink);
 
+/* The split-KV forward without its merge: the normalised partial O and the
+ * LSE of every split, in fp32, written to caller memory (the split-KV + merge
+ * plan of page "CURRENT ISSUE: UMMA FMHA — Full Pipeline + Production", "Next
+ * steps" item 4, with the merge left to the caller).  Several calls may write
+ * disjoint planes of one [n_parts, rows, hd] buffer, e.g. one call per key
+ * source, so that a single fmha_lse_merge combines all of them.
+ *  o_parts    fp32 [num_splits, B*T*n_h, hd]: plane i = attention over split
+ *             i's keys, normalised over them (O = 0 for a split without keys)
+ *  lse_parts  fp32 [num_splits, B*T*n_h], natural log (-inf: split without keys)
+ * Everything else as fmha_mqa_fwd (num_splits may be 1: one plane).
+ * o_parts 16-byte aligned, lse_parts 4-byte. */
+int fmha_mqa_fwd_partials(const void* q, const void* k, const void* v,
+                          const int32_t* kv_idx, float* o_parts, float* lse_parts,
+                          int B, int T, int n_h, int s_k, int hd, int pool_rows,
+                          float scale, int num_splits, void* stream);
+
 /* The same sink applied in place to finished rows (for results already merged
  * from several sources): for r in [0, rows), with h = r % n_h,
  *   lse[r] <- ln(exp(lse[r]) + exp(sink[h])),  out[r, :] *= exp(lse_old - lse_new).

@@ -33,8 +33,9 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["fmha_attention_sink", "fmha_gather_floor",
                                      "fmha_index_scores", "fmha_lse_merge", "fmha_mqa_fwd",
-                                     "fmha_mqa_fwd_sink", "fmha_mqa_workspace_bytes",
-                                     "fmha_status_string", "fmha_topk_select"]
+                                     "fmha_mqa_fwd_partials", "fmha_mqa_fwd_sink",
+                                     "fmha_mqa_workspace_bytes", "fmha_status_string",
+                                     "fmha_topk_select"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -233,3 +234,31 @@ def test_device_and_buffer_checks(F):
 ])
 def test_gather_floor_validates(F, args, status):
     assert F._binding._lib.fmha_gather_floor(*args) == status
+
+
+def _partials(F, **kw):
+    args = dict(q=A, k=A, v=A, kv_idx=None, o=A, l=A, B=1, T=1, n_h=1, s_k=8, hd=64,
+                pool_rows=0, scale=0.125, num_splits=1, stream=None)
+    args.update(kw)
+    return F._binding._lib.fmha_mqa_fwd_partials(
+        args["q"], args["k"], args["v"], args["kv_idx"], args["o"], args["l"], args["B"],
+        args["T"], args["n_h"], args["s_k"], args["hd"], args["pool_rows"], args["scale"],
+        args["num_splits"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 0),                     # nothing to compute
+    (dict(hd=96), 2),                   # unsupported head dim
+    (dict(o=None), 1),                  # partial planes missing
+    (dict(l=None), 1),
+    (dict(num_splits=0), 1),
+    (dict(num_splits=9, s_k=8), 1),     # more splits than keys
+    (dict(scale=0.0), 1),
+    (dict(o=A + 4), 3),                 # o_parts not 16-byte aligned
+    (dict(l=A + 2), 3),                 # lse_parts not 4-byte aligned
+    (dict(kv_idx=A, pool_rows=0), 1),   # gather without a pool
+])
+def test_partials_validates_before_launch(F, kw, status):
+    """fmha_mqa_fwd_partials rejects bad arguments with the documented status
+    (no device is touched: every pointer here is a fake address)."""
+    assert _partials(F, **kw) == status

@@ -110,6 +110,39 @@ def test_split_kv(F, splits, hd):
     _case(F, w)
 
 
+@pytest.mark.parametrize("hd,pool,s_k,splits", [(128, 0, 300, 3), (512, 0, 300, 3),
+                                                (128, 2048, 333, 4), (512, 2048, 333, 4),
+                                                (64, 0, 9, 8), (256, 700, 9, 8)])
+def test_partials_entry_point_planes_are_the_splits(F, hd, pool, s_k, splits):
+    """fmha_mqa_fwd_partials: plane i is attention over split i's keys alone
+    (contiguous chunks of ceil(s_k / splits); a split without keys gives O = 0,
+    lse = -inf), and the planes merged equal attention over all keys."""
+    w = W.make_custom(B=2, T=2, n_h=48, hd=hd, s_k=s_k, pool=pool, out_dtype="f32",
+                      num_splits=splits, seed=hd + s_k + splits)
+    q, k, v, idx = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    o_parts, l_parts = F.fwd_partials(q.to(dev), k.to(dev), v.to(dev),
+                                      None if idx is None else idx.to(dev), scale=w.scale,
+                                      num_splits=splits)
+    torch.cuda.synchronize()
+    c = -(-s_k // splits)
+    for i in range(splits):
+        lo, hi = min(i * c, s_k), min((i + 1) * c, s_k)
+        if hi <= lo:
+            assert torch.all(o_parts[i] == 0) and torch.all(torch.isneginf(l_parts[i]))
+            continue
+        if idx is None:
+            ks, vs, ids = k[:, lo:hi].contiguous(), v[:, lo:hi].contiguous(), None
+        else:
+            ks, vs, ids = k, v, idx[:, :, lo:hi].contiguous()
+        _check(o_parts[i], l_parts[i], q, ks, vs, ids, w.scale)
+    rows = w.B * w.T * w.n_h
+    out, lse = F.lse_merge(o_parts.view(splits, rows, hd), l_parts.view(splits, rows),
+                           torch.float32)
+    torch.cuda.synchronize()
+    _check(out.view(w.B, w.T, w.n_h, hd), lse.view(w.B, w.T, w.n_h), q, k, v, idx, w.scale)
+
+
 @pytest.mark.parametrize("hd,pool", [(128, 0), (512, 0), (128, 300), (512, 300)])
 def test_split_with_empty_trailing_chunks(F, hd, pool):
     # 9 keys in 8 chunks of 2: chunks 5..7 are empty (lse -inf) and must vanish
