@@ -260,6 +260,18 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(const float* __restri
   for (int i = n + tid; i < top_k; i += SEL_THREADS) dst[i] = -1;
   if (n <= 0) return;
 
+  // The histograms are cleared before the row is loaded, so that pass 1 can
+  // count each key as soon as its own load has landed (the loads return in
+  // order) while the later loads are still in flight.
+  const int pad = SEL_MAX_P - P;
+#pragma unroll
+  for (int b = 0; b < SEL_BINS / SEL_THREADS; ++b) {
+    histA[b * SEL_THREADS + tid] = 0;
+    histB[b * SEL_THREADS + tid] = 0;
+  }
+  if (tid == 0) s_ncand = 0;
+  __syncthreads();
+
   // key j of this thread is entry j * SEL_THREADS + tid (coalesced loads).
   // Buffer loads (past the row's end they read zero) with one shared 32-bit
   // offset: no predication and no per-load address, so all SEL_J loads are in
@@ -276,26 +288,16 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(const float* __restri
   // after every real entry, so the compaction never selects them.
   const int jn = (P - tid + SEL_THREADS - 1) / SEL_THREADS;  // this thread's real keys
   const int jfull = P / SEL_THREADS;                         // chunks real for every thread
-#pragma unroll
-  for (int j = 0; j < SEL_J; ++j) u[j] = order_key(__uint_as_float(u[j]));
-  if (jfull < SEL_J) {
-#pragma unroll
-    for (int j = 0; j < SEL_J; ++j)
-      if (j >= jfull) u[j] = j < jn ? u[j] : 0u;
-  }
-  const int pad = SEL_MAX_P - P;
-#pragma unroll
-  for (int b = 0; b < SEL_BINS / SEL_THREADS; ++b) {
-    histA[b * SEL_THREADS + tid] = 0;
-    histB[b * SEL_THREADS + tid] = 0;
-  }
-  if (tid == 0) s_ncand = 0;
-  __syncthreads();
 
-  // pass 1: bits 31..20 of every key
+  // pass 1: bits 31..20 of every key, each counted as it arrives
   if (tid == 0) atomicAdd(&histA[0], -pad);
 #pragma unroll
-  for (int j = 0; j < SEL_J; ++j) atomicAdd(&histA[u[j] >> 20], 1);
+  for (int j = 0; j < SEL_J; ++j) {
+    uint32_t key = order_key(__uint_as_float(u[j]));
+    if (j >= jfull && j >= jn) key = 0u;
+    u[j] = key;
+    atomicAdd(&histA[key >> 20], 1);
+  }
   __syncthreads();
   radix_step<SEL_BINS>(histA, wtot, s_sel, 0u, 20, n);
   uint32_t prefix = s_sel[0];
