@@ -432,7 +432,6 @@ void fwd_gather_staged_kernel(FwdParams p) {
   };
 
   Rows<HD, QW> w;
-  w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf);
   const float c = p.scale_log2;
   const int jj = lane & 15;
   const int dsub = (lane >> 4) & 1;
@@ -464,11 +463,22 @@ void fwd_gather_staged_kernel(FwdParams p) {
     barrier();
   };
 
-  // the split's index list, validated, as pool byte offsets
-  for (int i = tid; i < n_tiles * KT; i += 256) {
-    int idx = -1;
-    if (i < nk) idx = ibase[i];
-    sOff[i] = (idx >= 0 && idx < p.pool_rows) ? (uint32_t)idx * ROW : OOB;
+  // the split's index list, validated, as pool byte offsets: every entry of
+  // this thread is loaded before any is stored, so the loads (and Q's after
+  // them) are in flight together
+  constexpr int IPT = GSW_MAX_KEYS / 256;  // list entries per thread
+  int idxv[IPT];
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const int i = tid + 256 * e;
+    idxv[e] = i < nk ? ibase[i] : -1;
+  }
+  w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf);
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const int i = tid + 256 * e;
+    if (i < n_tiles * KT)
+      sOff[i] = (idxv[e] >= 0 && idxv[e] < p.pool_rows) ? (uint32_t)idxv[e] * ROW : OOB;
   }
   // Q and the list are in before any DMA is issued, so the compiler's own
   // waits for them stay out of the loop
