@@ -589,6 +589,20 @@ def main():
         del case
         torch.cuda.empty_cache()
 
+    # the two correctness configs (one KV tile; two KV tiles of one head):
+    # launch-latency bound, reported as time per call only
+    small = {}
+    for name, cid in (("single_head_decode", 1), ("single_head_prefill", 2)):
+        case = Case(cid, dev)
+        t = time_case(case, args.steps, args.warmup, flush_buf)
+        small[name] = {"us_per_call": round(t["ms"] * 1e3, 2),
+                       "us_median": round(t["ms_median"] * 1e3, 2),
+                       "us_per_call_warm": round(t["ms_warm"] * 1e3, 2),
+                       "workload": case.w.describe()}
+        print(f"[bench] {name}: {small[name]['us_per_call']:.1f} us/call flushed "
+              f"({small[name]['us_per_call_warm']:.1f} warm)", file=sys.stderr, flush=True)
+        del case
+
     # the widened rows: head dim 512 (decode split and Flash top-k), the
     # attention sink fused into decode, attention over two key sources
     nxt = {}
@@ -666,6 +680,7 @@ def main():
                         "us_p10": round(s["ms_p10"] * 1e3, 2), "us_p90": round(s["ms_p90"] * 1e3, 2),
                         "us_per_call_warm": round(s["ms_warm"] * 1e3, 2),
                         "workload": s["workload"]},
+        "small_configs": small,
         "prefill_detail": {"us_per_call": round(p["ms"] * 1e3, 2),
                            "us_median": round(p["ms_median"] * 1e3, 2),
                            "us_p10": round(p["ms_p10"] * 1e3, 2),
