@@ -38,11 +38,13 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 FLUSH_BYTES = 512 << 20
 
-# Sources the committed HBM traffic counters were taken on; a changed kernel
-# source makes those counters stale and the traffic field null.
-KERNEL_SOURCES = ["fmha_mqa_fwd_amd/csrc/fmha_fwd.hip", "fmha_mqa_fwd_amd/csrc/fmha_chunk.hip",
-                  "fmha_mqa_fwd_amd/csrc/lse_merge.hip", "fmha_mqa_fwd_amd/csrc/fmha_device.h",
-                  "fmha_mqa_fwd_amd/csrc/fmha_hd512.hip"]
+# Sources the committed HBM traffic counters were taken on: every HIP source
+# and header of the library (the ABI layer picks tile shapes and partial
+# formats, so it can change the traffic too).  A changed source makes those
+# counters stale and the traffic field null.
+CSRC_DIR = os.path.join(ROOT, "fmha_mqa_fwd_amd", "csrc")
+KERNEL_SOURCES = sorted(os.path.relpath(os.path.join(CSRC_DIR, f), ROOT)
+                        for f in os.listdir(CSRC_DIR) if f.endswith((".hip", ".h")))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # which attention kernels (by demangled name) serve each workload
 WORKLOAD_KERNEL_SIG = {

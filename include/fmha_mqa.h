@@ -7,9 +7,13 @@
  * between calls, and launches all work asynchronously on the given stream
  * (a hipStream_t passed as void*; NULL = the default stream).  Tensors are
  * row-major and contiguous.  No C++ exception crosses this boundary: every
- * function returns an fmha_status code, and validation happens before any
- * launch (a non-OK status means nothing was enqueued).  Device faults, as for
- * any HIP work, surface at the caller's next synchronisation.
+ * function returns an fmha_status code.  Validation happens before any launch:
+ * a validation error (FMHA_ERR_INVALID_ARG, _UNSUPPORTED, _ALIGNMENT,
+ * _WORKSPACE) means nothing was enqueued.  FMHA_ERR_LAUNCH means the HIP
+ * runtime refused a launch; when a call makes several launches, the ones
+ * before it may already be on the stream (they write only the caller's
+ * workspace or outputs).  Device faults, as for any HIP work, surface at the
+ * caller's next synchronisation.
  *
  * The operation is the fused attention forward of a DeepSeek-V4-style decoder
  * as described on the dev-log pages of the "nvfp4-megamoe-kernel" project:
@@ -47,7 +51,7 @@ extern "C" {
 typedef enum {
   FMHA_OK = 0,
   FMHA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad dtype/scale/splits */
-  FMHA_ERR_UNSUPPORTED = 2, /* head dim not in {64, 128, 256}; more than 2^31-1 rows;
+  FMHA_ERR_UNSUPPORTED = 2, /* head dim not in {64, 128, 256, 512}; more than 2^31-1 rows;
                                K/V (s_k rows dense, pool_rows gather) over 2 GiB */
   FMHA_ERR_ALIGNMENT = 3,   /* a tensor pointer not 16-byte aligned (lse: 4-byte) */
   FMHA_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned */

@@ -66,6 +66,21 @@ def F():
 A = 1 << 20
 
 
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+# The cases that hand the C entry points fake device addresses run only where
+# no GPU is visible: should validation ever regress, no kernel can then be
+# launched on an unmapped address.
+fake_pointers = pytest.mark.skipif(_gpu_visible(),
+                                   reason="passes fake device addresses: host-only check")
+
+
 def _fwd(F, **kw):
     args = dict(q=A, k=A, v=A, kv_idx=None, out=A, lse=A, B=1, T=1, n_h=1, s_k=8, hd=64,
                 pool_rows=0, scale=0.125, out_dtype=0, num_splits=1, ws=None, ws_bytes=0,
@@ -83,6 +98,7 @@ def test_status_strings(F):
     assert F.status_string(99) == "unknown status"
 
 
+@fake_pointers
 @pytest.mark.parametrize("kw,status", [
     (dict(hd=96), 2), (dict(hd=1024), 2), (dict(hd=0), 2),
     (dict(out_dtype=2), 1), (dict(B=-1), 1), (dict(s_k=-1), 1), (dict(num_splits=0), 1),
@@ -99,6 +115,7 @@ def test_fwd_rejects_bad_arguments(F, kw, status):
     assert _fwd(F, **kw) == status
 
 
+@fake_pointers
 @pytest.mark.parametrize("kw", [dict(B=0), dict(T=0), dict(n_h=0, q=None, out=None)])
 def test_fwd_empty_problem_is_a_no_op(F, kw):
     # zero rows: nothing to launch, OK even with dangling pointers
@@ -115,6 +132,7 @@ def test_workspace_bytes(F):
     assert F.workspace_bytes(-1, 1, 1, 64, 2) == 0
 
 
+@fake_pointers
 @pytest.mark.parametrize("args,status", [
     ((A, A, 0, 4, 64, A, 0, A, None), 1),      # n_parts < 1
     ((A, A, 2, 4, 62, A, 0, A, None), 1),      # hd not a multiple of 4
@@ -130,6 +148,7 @@ def test_merge_rejects_bad_arguments(F, args, status):
 
 
 # ------------------------------------------------------------ attention sink
+@fake_pointers
 def test_fwd_sink_requires_a_sink(F):
     lib = F._binding._lib
     args = (A, A, A, None, A, A, 1, 1, 1, 8, 64, 0, 0.125, 0, 1, None, 0, None)
@@ -139,6 +158,7 @@ def test_fwd_sink_requires_a_sink(F):
     assert lib.fmha_mqa_fwd_sink(*bad, A) == 2               # same checks as the plain forward
 
 
+@fake_pointers
 @pytest.mark.parametrize("args,status", [
     ((A, A, A, 4, 1, 64, 2, None), 1),       # bad dtype
     ((A, A, A, -1, 1, 64, 0, None), 1),
@@ -168,10 +188,12 @@ def test_attention_sink_validates(F, args, status):
     ((A, A, A, A + 2, 1, 2, 64, 128, 100, None), 3),
     ((None, None, None, None, 0, 5, 64, 128, 100, None), 0),  # no tokens: no-op
 ])
+@fake_pointers
 def test_index_scores_validates(F, args, status):
     assert F._binding._lib.fmha_index_scores(*args) == status
 
 
+@fake_pointers
 @pytest.mark.parametrize("args,status", [
     ((A, A, 4, 0, 8, None), 1),
     ((A, A, 4, 100, 0, None), 1),
@@ -224,6 +246,7 @@ def test_device_and_buffer_checks(F):
             B._check_buf("out", bad, (2, 3, 4, 8), (torch.float32,))
 
 
+@fake_pointers
 @pytest.mark.parametrize("args,status", [
     ((A, A, A, A, 1, 2, 64, 100, 0, None), 1),      # empty pool
     ((A, A, A, A, 1, 2, 64, 96, 10, None), 2),      # head dim
@@ -246,6 +269,7 @@ def _partials(F, **kw):
         args["num_splits"], args["stream"])
 
 
+@fake_pointers
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 0),                     # nothing to compute
     (dict(hd=96), 2),                   # unsupported head dim

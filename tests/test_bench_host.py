@@ -100,10 +100,10 @@ def test_committed_traffic_is_null_once_a_kernel_source_changes(tmp_path, monkey
     assert bench.committed_traffic("mqa_prefill") is None
 
 
-def test_the_hash_covers_every_attention_kernel_source():
-    """Every source build.py compiles is either hashed with the committed
-    counters or listed here as one that cannot change the attention kernels'
-    traffic (the indexer, the gather-only floor, the host-side ABI layer)."""
+def test_the_hash_covers_every_library_source():
+    """Every source build.py compiles, and every header beside them, is
+    hashed with the committed counters: any change to the library's code
+    turns them stale."""
     import importlib.util
     spec = importlib.util.spec_from_file_location(
         "fmha_mqa_build_for_test", os.path.join(bench.ROOT, "fmha_mqa_fwd_amd", "build.py"))
@@ -112,7 +112,7 @@ def test_the_hash_covers_every_attention_kernel_source():
     hashed = {os.path.basename(p) for p in bench.KERNEL_SOURCES}
     for rel in bench.KERNEL_SOURCES:
         assert os.path.exists(os.path.join(bench.ROOT, rel)), rel
-    not_hashed = {"api.hip", "fmha_indexer.hip", "gather_floor.hip"}
     for src in mod.SOURCES:
-        assert src in hashed or src in not_hashed, src
-    assert "fmha_device.h" in hashed
+        assert src in hashed, src
+    for hdr in ("fmha_device.h", "fmha_internal.h", "api.hip"):
+        assert hdr in hashed, hdr

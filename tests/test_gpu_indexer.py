@@ -112,23 +112,23 @@ def test_selected_lists_feed_the_sparse_attention(F):
     assert m["max_abs"] <= 1e-2 and m["min_row_cos"] >= 0.9999 and m["lse_err"] <= 1e-3, m
 
 
-def test_indexer_at_the_benchmarked_size_sampled(F):
+def test_indexer_at_the_benchmarked_size_all_tokens(F):
     """The shape bench.py times (B=4, T=512, 64 index heads x 128, a
-    32768-entry pool, top-k 1024): sampled tokens' scores against float64,
-    and their selections bit-exact against the exact top-k of the GPU's own
-    fp32 scores."""
+    32768-entry pool, top-k 1024): every token's scores against float64, and
+    every selection bit-exact against the exact top-k of the GPU's own fp32
+    scores (the selection is decided in the kernel's precision)."""
     B, T, H, c, P, top_k = 4, 512, 64, 128, 32768, 1024
     q, k, w = _inputs(B, T, H, c, P, seed=4001)
     qd, kd, wd = q.to(DEV), k.to(DEV), w.to(DEV)
     s = F.index_scores(qd, kd, wd)
     idx = F.topk_select(s, top_k)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(7)
-    toks = [(int(b), int(t)) for b, t in zip(rng.integers(0, B, 6), rng.integers(0, T, 6))]
-    toks += [(0, 0), (B - 1, T - 1)]
-    for b, t in toks:
-        ref = OI.index_scores(q[b:b + 1, t:t + 1], k, w[b:b + 1, t:t + 1])[0, 0]
-        got = s[b, t].cpu().numpy()
-        assert np.all(np.abs(got - ref) <= 1e-5 * (np.abs(ref).max() + 1.0)), (b, t)
-        want = OI.topk_select(got.astype(np.float64)[None], top_k)[0]
-        assert np.array_equal(idx[b, t].cpu().numpy().astype(np.int64), want), (b, t)
+    got_all = s.cpu().numpy()
+    idx_all = idx.cpu().numpy().astype(np.int64)
+    for b in range(B):
+        ref = OI.index_scores(q[b:b + 1], k, w[b:b + 1])[0]          # [T, P] float64
+        got = got_all[b]
+        tol = 1e-5 * (np.abs(ref).max(axis=1, keepdims=True) + 1.0)
+        assert np.all(np.abs(got - ref) <= tol), b
+        want = OI.topk_select(got.astype(np.float64), top_k)
+        assert np.array_equal(idx_all[b], want), b

@@ -84,19 +84,13 @@ def test_decode_shape_two_sources(F):
     _check(out, lse, q, [top, win], scale)
 
 
-def test_two_sources_benchmarked_size_sampled(F):
+def test_two_sources_benchmarked_size_all_rows(F):
     """The multi-source row as bench.py times it: B=32, 64 heads, hd 512,
     top-k 512 of a 32768-row pool (8 splits) plus a 128-key window (4 splits),
-    bf16 out; rows sampled against the one-softmax oracle."""
+    bf16 out; every row against the one-softmax oracle."""
     q, top, win, scale = _inputs(B=32, T=1, n_h=64, hd=512, pool=32768, top_k=512, window=128,
                                  seed=98)
     out, lse = F.fwd_sources(q.to(DEV), [_d(top, 8), _d(win, 4)], scale=scale,
                              out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    rows = np.concatenate([[0, 32 * 64 - 1], np.random.default_rng(9).choice(32 * 64, 200,
-                                                                            replace=False)])
-    O_ref, L_ref = oracle.attention_sources(q, [top, win], scale, rows=rows)
-    ri = torch.as_tensor(rows, device=out.device)
-    m = oracle.row_metrics(out.float().reshape(-1, 512)[ri].cpu().numpy(), O_ref,
-                           lse.reshape(-1)[ri].cpu().numpy(), L_ref)
-    assert m["max_abs"] <= MAX_ABS and m["min_row_cos"] >= MIN_COS and m["lse_err"] <= LSE_ERR, m
+    _check(out, lse, q, [top, win], scale)

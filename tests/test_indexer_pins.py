@@ -82,11 +82,26 @@ def test_selection_pads_short_pools():
 
 
 def test_planted_mistakes_fail_a_pin():
+    """Four plausible misreadings, each swapped into the oracle in turn, must
+    each fail at least one pin: the ReLU dropped, the ReLU applied after the
+    head weighting, the selection listed in descending id order, and ties
+    broken towards the larger id."""
     good_scores, good_sel = I.index_scores, I.topk_select
 
     def no_relu(q, k, w):
         q, k, w = (x.double().numpy() for x in (q, k, w))
         return np.einsum("bth,bthp->btp", w, q @ k.T)
+
+    def relu_after_weighting(q, k, w):
+        q, k, w = (x.double().numpy() for x in (q, k, w))
+        return np.maximum(w[..., None] * (q @ k.T), 0.0).sum(axis=2)
+
+    def descending_ids(scores, top_k):
+        sel = good_sel(scores, top_k)
+        n = min(top_k, np.shape(scores)[-1])
+        out = sel.copy()
+        out[..., :n] = sel[..., :n][..., ::-1]
+        return out
 
     def ties_to_larger(scores, top_k):
         s = np.asarray(scores, np.float64)
@@ -97,17 +112,22 @@ def test_planted_mistakes_fail_a_pin():
             out.append(sorted(order) + [-1] * (top_k - len(order)))
         return np.array(out).reshape(*s.shape[:-1], top_k)
 
-    for name, patch in (("index_scores", no_relu), ("topk_select", ties_to_larger)):
+    pins = (lambda: test_scores_match_brute_force(2, 3, 4, 8, 7),
+            test_one_hot_weight_picks_one_head_relu,
+            test_nonnegative_inputs_make_the_score_linear,
+            test_selection_matches_torch_topk_on_distinct_scores,
+            test_selection_ties_go_to_the_smaller_id,
+            test_selection_pads_short_pools)
+    for name, patch in (("index_scores", no_relu), ("index_scores", relu_after_weighting),
+                        ("topk_select", descending_ids), ("topk_select", ties_to_larger)):
         setattr(I, name, patch)
         try:
             caught = 0
-            for chk in (lambda: test_scores_match_brute_force(2, 3, 4, 8, 7),
-                        test_one_hot_weight_picks_one_head_relu,
-                        test_selection_ties_go_to_the_smaller_id):
+            for chk in pins:
                 try:
                     chk()
                 except AssertionError:
                     caught += 1
-            assert caught >= 1, f"planted mistake in {name} passed every pin"
+            assert caught >= 1, f"planted mistake {patch.__name__} passed every pin"
         finally:
             I.index_scores, I.topk_select = good_scores, good_sel

@@ -29,6 +29,50 @@ def _tolist(a):
     return np.asarray(a).tolist()
 
 
+# ------------------------------------------------------- the input conversion
+def _decode_bf16(bits: int) -> float:
+    """bf16 value of a 16-bit pattern from its fields (IEEE-754 binary16-brain:
+    1 sign, 8 exponent bits with bias 127, 7 fraction bits), with no library
+    conversion involved."""
+    sign = -1.0 if bits & 0x8000 else 1.0
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if f == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(f, -133)          # subnormal: f * 2^(1 - 127 - 7)
+    return sign * math.ldexp(128 + f, e - 134)     # (1 + f/128) * 2^(e - 127)
+
+
+def test_to_f64_is_the_exact_bf16_value():
+    """The oracle reads bf16 inputs through to_f64; every pattern class —
+    signed zeros, subnormals, the smallest normal, the largest finite value,
+    infinities and ordinary values — must arrive as its exact value."""
+    named = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x3F80, 0xBF80, 0x4049,
+             0x7F7F, 0xFF7F, 0x7F80, 0xFF80, 0x3C00, 0x4780]
+    rng = np.random.default_rng(11)
+    finite = [int(b) for b in rng.integers(0, 1 << 16, 4000) if ((int(b) >> 7) & 0xFF) != 0xFF]
+    pats = named + finite
+    t = torch.tensor([b - (1 << 16) if b >= 1 << 15 else b for b in pats],
+                     dtype=torch.int16).view(torch.bfloat16)
+    got = oracle.to_f64(t)
+    assert got.dtype == np.float64
+    want = [_decode_bf16(b) for b in pats]
+    for b, g_, w in zip(pats, got.tolist(), want):
+        assert g_ == w, hex(b)
+        assert math.copysign(1.0, g_) == math.copysign(1.0, w), hex(b)  # -0 stays -0
+    assert got[named.index(0x0001)] == 2.0 ** -133
+    assert got[named.index(0x7F7F)] == (2 - 2 ** -7) * 2.0 ** 127
+    # integer index lists keep their exact values, as an integer dtype
+    idx = torch.tensor([0, 1, 32767, -1, 2 ** 31 - 1, -2 ** 31], dtype=torch.int32)
+    gi = oracle.to_f64(idx)
+    assert gi.dtype.kind == "i" and gi.tolist() == [0, 1, 32767, -1, 2 ** 31 - 1, -2 ** 31]
+    # fp32 inputs (sinks) arrive exactly too
+    f = torch.tensor([1.0 / 3.0, -2.5e-40, 3.0e38], dtype=torch.float32)
+    assert oracle.to_f64(f).tolist() == [float(np.float32(x)) for x in (1.0 / 3.0, -2.5e-40,
+                                                                        3.0e38)]
+
+
 # ---------------------------------------------------------------- brute force
 @pytest.mark.parametrize("B,T,n_h,s_k,hd", [
     (1, 1, 1, 1, 1), (1, 2, 3, 2, 3), (2, 3, 2, 5, 8), (3, 1, 2, 9, 3),
