@@ -7,7 +7,6 @@ prefill, decode and sparse top-k workloads and the head-dim-512 rows at their
 benchmarked sizes included.
 """
 import math
-import sys
 
 import numpy as np
 import pytest
@@ -15,6 +14,7 @@ import torch
 
 import oracle
 import workloads as W
+from conftest import say
 
 pytestmark = pytest.mark.gpu
 
@@ -60,11 +60,9 @@ def _case(F, w, rows=None):
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
     m = _check(out, lse, q, k, v, idx, w.scale, rows=rows)
     # the measured margins, on the real stderr (pytest captures stdout)
-    sys.__stderr__.write(f"[parity] {w.describe()}"
-                         f"{'' if rows is None else f' ({len(rows)} sampled rows)'}: "
-                         f"max_abs {m['max_abs']:.3e} min_row_cos {m['min_row_cos']:.7f} "
-                         f"lse_err {m['lse_err']:.3e}\n")
-    sys.__stderr__.flush()
+    say(f"[parity] {w.describe()}{'' if rows is None else f' ({len(rows)} sampled rows)'}: "
+        f"max_abs {m['max_abs']:.3e} min_row_cos {m['min_row_cos']:.7f} "
+        f"lse_err {m['lse_err']:.3e}")
     return m
 
 
