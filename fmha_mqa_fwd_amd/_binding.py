@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfmha_mqa
 
 FMHA_F32 = 0
 FMHA_BF16 = 1
+FMHA_ERR_SCRATCH_LIMIT = 6
+SCRATCH_BYTES = 64 << 20   # FMHA_SCRATCH_BYTES: the static split-KV buffer per GPU
 
 # Every symbol include/fmha_mqa.h declares, with its ctypes signature.
 _c_int, _c_size, _c_void_p, _c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -26,6 +28,9 @@ SIGNATURES = {
     "fmha_mqa_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                               _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                               _c_int, _c_int, _c_void_p, _c_size, _c_void_p]),
+    "fmha_mqa_fwd_noalloc": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                      _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                      _c_float, _c_int, _c_int, _c_void_p]),
     "fmha_mqa_fwd_sink": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                    _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_float, _c_int, _c_int, _c_void_p, _c_size, _c_void_p,
@@ -127,7 +132,8 @@ class FwdPlan:
     With partials=True the plan calls fmha_mqa_fwd_partials instead: out and
     lse are then the fp32 split planes [num_splits, B, T, n_h, hd] and
     [num_splits, B, T, n_h] (allocated when None); out_dtype, workspace and
-    sink do not apply.
+    sink do not apply.  With noalloc=True it calls fmha_mqa_fwd_noalloc: out
+    and lse must be given, and there is no workspace or sink.
     """
 
     def __init__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -135,7 +141,8 @@ class FwdPlan:
                  out_dtype: torch.dtype = torch.bfloat16, num_splits: int = 1,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None, stream=None,
-                 sink: Optional[torch.Tensor] = None, partials: bool = False):
+                 sink: Optional[torch.Tensor] = None, partials: bool = False,
+                 noalloc: bool = False):
         if q.dim() != 4:
             raise ValueError("q must be [B, T, n_h, hd]")
         B, T, n_h, hd = q.shape
@@ -184,6 +191,21 @@ class FwdPlan:
             _check_buf("out", out, (B, T, n_h, hd), (torch.float32, torch.bfloat16))
         if lse is not None:
             _check_buf("lse", lse, (B, T, n_h), (torch.float32,))
+        if noalloc:
+            if sink is not None or workspace is not None:
+                raise ValueError("the allocation-free forward takes neither a sink nor a "
+                                 "workspace")
+            if out is None or lse is None:
+                raise ValueError("the allocation-free forward writes into the caller's out "
+                                 "and lse")
+            self._keep = (q, k, v, kv_idx)
+            self.out, self.lse = out, lse
+            self._fn = _lib.fmha_mqa_fwd_noalloc
+            self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(out), _ptr(lse),
+                          B, T, n_h, s_k, hd, pool_rows,
+                          float(default_scale(hd) if scale is None else scale),
+                          _dtype_code(out.dtype), int(num_splits), _stream_handle(stream))
+            return
         if workspace is not None and not workspace.is_contiguous():
             raise ValueError("workspace must be contiguous")
         if scale is None:
@@ -229,6 +251,18 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """
     return FwdPlan(q, k, v, kv_idx, scale, out_dtype, num_splits, out, lse, workspace, stream,
                    sink)()
+
+
+def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                lse: torch.Tensor, kv_idx: Optional[torch.Tensor] = None,
+                scale: Optional[float] = None, num_splits: int = 1, stream=None
+                ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fmha_mqa_fwd_noalloc: the forward into the caller's out [B, T, n_h, hd]
+    (fp32 or bf16) and lse [B, T, n_h] fp32 with no workspace — split-KV
+    partials live in the library's static per-GPU scratch buffer, and nothing
+    is allocated here either.  Arguments otherwise as for `fwd`."""
+    return FwdPlan(q, k, v, kv_idx, scale, out.dtype, num_splits, out, lse, stream=stream,
+                   noalloc=True)()
 
 
 def fwd_partials(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

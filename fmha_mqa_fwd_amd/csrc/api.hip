@@ -9,8 +9,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fmha_internal.h"
 #include "fmha_mqa.h"
+
+// Scratch memory of fmha_mqa_fwd_noalloc: the split-KV workspace for callers
+// that cannot allocate.  Each GPU the library runs on holds its own copy for
+// the life of the process.  In host code `scratch` names a host-side stand-in,
+// never the device memory: kernels and copies use the per-device address that
+// hipGetSymbolAddress returns (scratch_address below).
+static __device__ __align__(256) char scratch[FMHA_SCRATCH_BYTES];
 
 namespace {
 
@@ -40,10 +49,13 @@ inline int launch_status(hipError_t e) { return e == hipSuccess ? FMHA_OK : FMHA
 // and, with partials_only, of fmha_mqa_fwd_partials: out/lse are then the
 // caller's fp32 partial planes [num_splits, rows, hd] / [num_splits, rows],
 // written without a merge (out_dtype, sink and workspace unused).
+// validate_only: return the validation status without launching anything
+// (the workspace is not looked at).
 int fwd_impl(const void* q, const void* k, const void* v, const int32_t* kv_idx, void* out,
              float* lse, int B, int T, int n_h, int s_k, int hd, int pool_rows, float scale,
              int out_dtype, int num_splits, void* workspace, size_t workspace_bytes,
-             void* stream, const float* sink, bool partials_only = false) {
+             void* stream, const float* sink, bool partials_only = false,
+             bool validate_only = false) {
   if (out_dtype != FMHA_F32 && out_dtype != FMHA_BF16) return FMHA_ERR_INVALID_ARG;
   if (B < 0 || T < 0 || n_h < 0 || s_k < 0 || num_splits < 1) return FMHA_ERR_INVALID_ARG;
   if (hd != 64 && hd != 128 && hd != 256 && hd != 512) return FMHA_ERR_UNSUPPORTED;
@@ -86,6 +98,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* kv_idx,
 
   const int64_t grid = fmha::fwd_grid_size(p, hd);
   if (grid > INT32_MAX) return FMHA_ERR_UNSUPPORTED;
+  if (validate_only) return FMHA_OK;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // launch errors below are ours alone
@@ -122,6 +135,35 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* kv_idx,
                                           bf16_parts));
 }
 
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of `scratch` on the GPU that runs `stream`, looked up
+// once per device with that device current.  nullptr if the lookup failed.
+void* scratch_address(hipStream_t stream) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    int prev = -1;
+    g_scratch_err[dev] = hipGetDevice(&prev);
+    if (g_scratch_err[dev] != hipSuccess) return;
+    if (prev != dev) g_scratch_err[dev] = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (g_scratch_err[dev] == hipSuccess)
+      g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (g_scratch_err[dev] == hipSuccess) g_scratch_ptr[dev] = ptr;
+    if (prev != dev) (void)hipSetDevice(prev);
+  });
+  return g_scratch_err[dev] == hipSuccess ? g_scratch_ptr[dev] : nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,6 +190,26 @@ int fmha_mqa_fwd_sink(const void* q, const void* k, const void* v, const int32_t
   if (!sink) return FMHA_ERR_INVALID_ARG;
   return fwd_impl(q, k, v, kv_idx, out, lse, B, T, n_h, s_k, hd, pool_rows, scale, out_dtype,
                   num_splits, workspace, workspace_bytes, stream, sink);
+}
+
+int fmha_mqa_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* kv_idx,
+                         void* out, float* lse, int B, int T, int n_h, int s_k, int hd,
+                         int pool_rows, float scale, int out_dtype, int num_splits,
+                         void* stream) {
+  // every argument is checked before the device is touched
+  const int s = fwd_impl(q, k, v, kv_idx, out, lse, B, T, n_h, s_k, hd, pool_rows, scale,
+                         out_dtype, num_splits, nullptr, 0, stream, nullptr, false, true);
+  if (s != FMHA_OK) return s;
+  void* ws = nullptr;
+  const int64_t rows = (int64_t)B * T * n_h;
+  if (num_splits > 1 && rows > 0) {
+    if (ws_layout(rows, hd, num_splits).total > (size_t)FMHA_SCRATCH_BYTES)
+      return FMHA_ERR_SCRATCH_LIMIT;
+    ws = scratch_address(static_cast<hipStream_t>(stream));
+    if (ws == nullptr) return FMHA_ERR_LAUNCH;
+  }
+  return fwd_impl(q, k, v, kv_idx, out, lse, B, T, n_h, s_k, hd, pool_rows, scale, out_dtype,
+                  num_splits, ws, ws ? (size_t)FMHA_SCRATCH_BYTES : 0, stream, nullptr);
 }
 
 int fmha_mqa_fwd_partials(const void* q, const void* k, const void* v, const int32_t* kv_idx,
@@ -240,6 +302,8 @@ const char* fmha_status_string(int status) {
     case FMHA_ERR_ALIGNMENT: return "misaligned pointer";
     case FMHA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case FMHA_ERR_LAUNCH: return "kernel launch failed";
+    case FMHA_ERR_SCRATCH_LIMIT:
+      return "split-KV partials exceed the static scratch buffer (FMHA_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -55,8 +55,13 @@ typedef enum {
                                K/V (s_k rows dense, pool_rows gather) over 2 GiB */
   FMHA_ERR_ALIGNMENT = 3,   /* a tensor pointer not 16-byte aligned (lse: 4-byte) */
   FMHA_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned */
-  FMHA_ERR_LAUNCH = 5       /* the HIP runtime rejected a kernel launch */
+  FMHA_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch */
+  FMHA_ERR_SCRATCH_LIMIT = 6 /* fmha_mqa_fwd_noalloc: the split partials need more than
+                               FMHA_SCRATCH_BYTES */
 } fmha_status;
+
+/* Size of the library's static per-GPU scratch buffer (fmha_mqa_fwd_noalloc). */
+#define FMHA_SCRATCH_BYTES (64u << 20)
 
 typedef enum { FMHA_F32 = 0, FMHA_BF16 = 1 } fmha_dtype;
 
@@ -92,6 +97,25 @@ int fmha_mqa_fwd(const void* q, const void* k, const void* v,
                  int B, int T, int n_h, int s_k, int hd, int pool_rows,
                  float scale, int out_dtype, int num_splits,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* fmha_mqa_fwd for callers that cannot allocate device memory — code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc: the same
+ * forward without the workspace arguments.  A split-KV call (num_splits > 1)
+ * keeps its partials in a static buffer of FMHA_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on until the process ends; the call itself
+ * allocates nothing.  Arguments, layouts and results as fmha_mqa_fwd.
+ *  Limit: the partials (fmha_mqa_workspace_bytes(B, T, n_h, hd, num_splits)
+ *  bytes) must fit in FMHA_SCRATCH_BYTES, else FMHA_ERR_SCRATCH_LIMIT and
+ *  nothing is enqueued (e.g. B*T*n_h = 4096 rows at hd 256 allow 15 splits).
+ *  Every call on one GPU shares that GPU's buffer: calls that may overlap on
+ *  one GPU (different streams, or several host threads) race and must be
+ *  serialised by the caller; calls on one stream are ordered by it.
+ *  FMHA_ERR_LAUNCH is also returned if the buffer's device address cannot be
+ *  obtained (looked up once per GPU, on the first split-KV call there). */
+int fmha_mqa_fwd_noalloc(const void* q, const void* k, const void* v,
+                         const int32_t* kv_idx, void* out, float* lse,
+                         int B, int T, int n_h, int s_k, int hd, int pool_rows,
+                         float scale, int out_dtype, int num_splits, void* stream);
 
 /* fmha_mqa_fwd with an attention sink joined to every row (page "May 24, 2026 —
  * Session Start Plan" names a "sink merge" — File Map, D1 Status Summary D5b —

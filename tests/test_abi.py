@@ -33,7 +33,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["fmha_attention_sink", "fmha_gather_floor",
                                      "fmha_index_scores", "fmha_lse_merge", "fmha_mqa_fwd",
-                                     "fmha_mqa_fwd_partials", "fmha_mqa_fwd_sink",
+                                     "fmha_mqa_fwd_noalloc", "fmha_mqa_fwd_partials",
+                                     "fmha_mqa_fwd_sink",
                                      "fmha_mqa_workspace_bytes", "fmha_status_string",
                                      "fmha_topk_select"]
 
@@ -95,7 +96,38 @@ def _fwd(F, **kw):
 def test_status_strings(F):
     assert F.status_string(0) == "ok"
     assert "align" in F.status_string(3)
+    assert "scratch" in F.status_string(F.FMHA_ERR_SCRATCH_LIMIT)
     assert F.status_string(99) == "unknown status"
+
+
+def _noalloc(F, **kw):
+    args = dict(q=A, k=A, v=A, kv_idx=None, out=A, lse=A, B=1, T=1, n_h=1, s_k=8, hd=64,
+                pool_rows=0, scale=0.125, out_dtype=0, num_splits=1, stream=None)
+    args.update(kw)
+    return F._binding._lib.fmha_mqa_fwd_noalloc(
+        args["q"], args["k"], args["v"], args["kv_idx"], args["out"], args["lse"], args["B"],
+        args["T"], args["n_h"], args["s_k"], args["hd"], args["pool_rows"], args["scale"],
+        args["out_dtype"], args["num_splits"], args["stream"])
+
+
+@fake_pointers
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 0),                                   # nothing to compute
+    (dict(hd=96), 2), (dict(q=None), 1), (dict(num_splits=9), 1), (dict(q=A + 8), 3),
+    # partials over the 64 MiB buffer: 4096 rows x hd 256 x 16 splits (64.25 MiB)
+    (dict(B=32, n_h=128, hd=256, s_k=1024, num_splits=16), 6),
+    (dict(B=32, n_h=128, hd=512, s_k=1024, num_splits=8), 6),
+])
+def test_noalloc_validates_before_touching_the_device(F, kw, status):
+    """fmha_mqa_fwd_noalloc rejects bad arguments, and partials larger than its
+    static buffer, before any device call (every pointer here is fake)."""
+    assert _noalloc(F, **kw) == status
+
+
+def test_noalloc_limit_matches_the_workspace_size(F):
+    assert F.SCRATCH_BYTES == 64 << 20
+    assert F.workspace_bytes(32, 1, 128, 256, 15) <= F.SCRATCH_BYTES
+    assert F.workspace_bytes(32, 1, 128, 256, 16) > F.SCRATCH_BYTES
 
 
 @fake_pointers
