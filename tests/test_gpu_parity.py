@@ -145,6 +145,97 @@ def test_partials_entry_point_planes_are_the_splits(F, hd, pool, s_k, splits):
     _check(out.view(w.B, w.T, w.n_h, hd), lse.view(w.B, w.T, w.n_h), q, k, v, idx, w.scale)
 
 
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
+def test_split_workspace_contents_do_not_matter(F, hd, fill):
+    """Whatever the split-KV workspace held before (zero bytes, all-one bytes,
+    random bytes, or what a previous call left), the result is the same."""
+    w = W.make_custom(B=4, T=1, n_h=128, hd=hd, s_k=700, out_dtype="bf16", num_splits=6,
+                      seed=hd + len(fill))
+    q, k, v, idx = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    ws = torch.empty(F.workspace_bytes(w.B, w.T, w.n_h, w.hd, w.num_splits), dtype=torch.uint8,
+                     device=dev)
+    if fill == "zeros":
+        ws.zero_()
+    elif fill == "ones":
+        ws.fill_(0xFF)
+    else:
+        g = torch.Generator().manual_seed(hd)
+        ws.copy_(torch.randint(0, 256, ws.shape, generator=g, dtype=torch.uint8))
+    o1, l1 = F.fwd(qd, kd, vd, scale=w.scale, out_dtype=torch.bfloat16, num_splits=6, workspace=ws)
+    o2, l2 = F.fwd(qd, kd, vd, scale=w.scale, out_dtype=torch.bfloat16, num_splits=6, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    _check(o1, l1, q, k, v, None, w.scale)
+
+
+@pytest.mark.parametrize("n_h,T", [(1, 1), (37, 1), (100, 1), (65, 3)])
+@pytest.mark.parametrize("splits", [2, 5])
+def test_split_row_tiles_ragged(F, n_h, T, splits):
+    """Split-KV groups whose row count is not a multiple of a workgroup's row
+    tile (one row, part of one tile, one and a half tiles; dense groups of
+    T*n_h rows)."""
+    w = W.make_custom(B=3, T=T, n_h=n_h, hd=256, s_k=333, out_dtype="f32", num_splits=splits,
+                      seed=n_h * 10 + T + splits)
+    _case(F, w)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+def test_split_gather_masks_invalid_entries(F, hd):
+    """Gathered split-KV: invalid entries (-1, pool_rows, INT32_MAX) inside
+    splits, a split whose entries are all invalid and a token with one valid
+    entry give attention over the valid entries alone."""
+    P, s_k = 2000, 300
+    w = W.make_custom(B=1, T=3, n_h=64, hd=hd, s_k=s_k, pool=P, out_dtype="f32", num_splits=4,
+                      seed=91 + hd)
+    q, k, v, idx = W.make_inputs(w)
+    bad = idx.clone()
+    bad[0, 0, 3] = -1
+    bad[0, 0, 80:95] = P
+    bad[0, 0, 150:225] = 2 ** 31 - 1      # the whole third split (75 keys each)
+    bad[0, 1, ::7] = -5
+    bad[0, 2, :] = -1
+    bad[0, 2, 260] = idx[0, 2, 260]
+    out, lse = _run(F, q, k, v, bad, w.scale, torch.float32, 4)
+    for t in range(3):
+        ok = [int(bad[0, t, j]) for j in range(s_k) if 0 <= int(bad[0, t, j]) < P]
+        sub = torch.tensor([[ok]], dtype=torch.int32)
+        _check(out[:, t:t + 1], lse[:, t:t + 1], q[:, t:t + 1], k, v, sub, w.scale)
+
+
+def test_split_kv_replays_in_a_hip_graph(F):
+    """The split-KV forward (split kernel + merge kernel) captured in a HIP
+    graph: every replay, with the program's own eager work and
+    synchronisations between replays, gives the eager result bit for bit."""
+    w = W.make_custom(B=8, T=1, n_h=128, hd=256, s_k=1024, out_dtype="bf16", num_splits=8,
+                      seed=77)
+    q, k, v, _ = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    plan = F.FwdPlan(qd, kd, vd, scale=w.scale, out_dtype=torch.bfloat16, num_splits=8,
+                     stream=side)
+    with torch.cuda.stream(side):
+        ref_out, ref_lse = (t.clone() for t in plan())
+    side.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        plan()
+    for i in range(4):
+        plan.out.fill_(float("nan"))
+        plan.lse.fill_(float("nan"))
+        x = torch.randn(1 << 20, device=dev) * (i + 1)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.out, ref_out) and torch.equal(plan.lse, ref_lse), i
+        del x
+    _check(ref_out, ref_lse, q, k, v, None, w.scale)
+
+
 @pytest.mark.parametrize("hd,pool", [(128, 0), (512, 0), (128, 300), (512, 300)])
 def test_split_with_empty_trailing_chunks(F, hd, pool):
     # 9 keys in 8 chunks of 2: chunks 5..7 are empty (lse -inf) and must vanish
