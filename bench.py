@@ -147,6 +147,58 @@ class FloorCase:
         self.F.gather_floor(self.k, self.v, self.idx, out=self.out)
 
 
+class ReadFloorCase:
+    """The read floor of a dense split-KV workload: fmha_read_floor reads the
+    bytes the split kernel reads (its q rows and its split's K/V rows), with
+    the same workgroups and no arithmetic."""
+
+    def __init__(self, case):
+        self.F = case.F
+        self.q, self.k, self.v = case.q, case.k, case.v
+        w = case.w
+        self.splits = w.num_splits
+        n_wg = -(-(w.T * w.n_h) // 128) * w.B * w.num_splits
+        self.out = torch.empty((n_wg,), dtype=torch.int32, device=case.q.device)
+        self.bytes = w.rows * w.hd * 2 + 2 * w.B * w.s_k * w.hd * 2   # q once, K and V once
+
+    def __call__(self):
+        self.F.read_floor(self.q, self.k, self.v, self.splits, out=self.out)
+
+
+MFMA_ITERS = 20000   # ~2.5-3.5 ms per launch: long enough for the clock to settle
+
+
+def mfma_ceiling(dev, reps=20):
+    """Sustained bf16 matrix-core rate on random operands (fmha_mfma_ceiling,
+    one 8-wave workgroup per CU): median TFLOP/s over `reps` launches and the
+    median effective shader clock read in the kernel."""
+    import fmha_mqa_fwd_amd as F
+
+    g = torch.Generator().manual_seed(11)
+    ops = torch.randn(8, 8, 64, 8, generator=g).to(torch.bfloat16).to(dev)
+    n_wg = torch.cuda.get_device_properties(dev).multi_processor_count
+    flops = n_wg * 8 * 4 * MFMA_ITERS * 32768
+    sums = torch.empty((n_wg, 8, 4), dtype=torch.float32, device=dev)
+    clocks = torch.empty((n_wg, 2), dtype=torch.int64, device=dev)
+    for _ in range(5):
+        F.mfma_ceiling(ops, n_wg, MFMA_ITERS, sums=sums, clocks=clocks)
+    torch.cuda.synchronize()
+    ts, ghz = [], []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        F.mfma_ceiling(ops, n_wg, MFMA_ITERS, sums=sums, clocks=clocks)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+        c = clocks.cpu().double()
+        ghz.append(float((c[:, 0] / c[:, 1]).median()) * 0.1)
+    ts.sort()
+    ghz.sort()
+    return {"TFLOPs": flops / ts[len(ts) // 2] / 1e12, "clock_GHz": ghz[len(ghz) // 2],
+            "workgroups": n_wg, "us_per_launch": ts[len(ts) // 2] * 1e6}
+
+
 class SourcesCase:
     """Decode over two key sources — top-k rows gathered from a compressed
     pool plus a dense sliding window — in one softmax: one forward per source
@@ -578,6 +630,16 @@ def main():
         print(f"[bench] {name}: {t['ms'] * 1e3:.1f} us/call flushed "
               f"({t['ms_warm'] * 1e3:.1f} warm), {t['tflops']:.1f} TFLOP/s, "
               f"{t['gbps']:.0f} GB/s", file=sys.stderr, flush=True)
+        if name == "mqa_decode":
+            # the split kernel's reads alone: its q rows and its split's K/V rows
+            fl = ReadFloorCase(case)
+            tf = time_case(fl, args.steps, args.warmup, flush_buf)
+            t["read_floor_ms"], t["read_floor_ms_warm"] = tf["ms"], tf["ms_warm"]
+            t["read_floor_gbps"] = fl.bytes / (tf["ms"] * 1e-3) / 1e9
+            print(f"[bench] {name} read floor: {tf['ms'] * 1e3:.1f} us/call flushed "
+                  f"({tf['ms_warm'] * 1e3:.1f} warm), {t['read_floor_gbps']:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+            del fl
         if case.idx is not None:
             # the memory side's floor for the same gathered rows
             fl = FloorCase(case)
@@ -623,6 +685,12 @@ def main():
     for name, make in nxt_cases:
         case = make()
         t = time_case(case, args.steps, args.warmup, flush_buf)
+        floor = None
+        if isinstance(case, Case) and case.idx is not None:
+            fl = FloorCase(case)
+            floor = time_case(fl, args.steps, args.warmup, flush_buf)
+            floor["gbps"] = fl.bytes / (floor["ms"] * 1e-3) / 1e9
+            del fl
         if isinstance(case, (SourcesCase, IndexerCase)):
             flops, nbytes, desc = case.flops, case.bytes, case.desc
         else:
@@ -632,6 +700,11 @@ def main():
                "GBps": round(nbytes / (t["ms"] * 1e-3) / 1e9, 1), "workload": desc}
         ent["frac_of_mfma_peak"] = round(ent["TFLOPs"] / PEAK_BF16_TFLOPS, 4)
         ent["frac_of_hbm_peak"] = round(ent["GBps"] / PEAK_HBM_GBPS, 4)
+        if floor is not None:
+            # the gather-only floor of the same index lists (fmha_gather_floor)
+            ent["gather_floor_us"] = round(floor["ms"] * 1e3, 2)
+            ent["gather_floor_GBps"] = round(floor["gbps"], 1)
+            ent["floor_over_call"] = round(floor["ms"] / t["ms"], 4)
         nxt[name] = ent
         print(f"[bench] {name}: {ent['us_per_call']:.1f} us/call flushed, {ent['TFLOPs']:.1f} "
               f"TFLOP/s, {ent['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
@@ -640,6 +713,9 @@ def main():
 
     copy_gbps = copy_ceiling(dev)
     print(f"[bench] device copy: {copy_gbps:.0f} GB/s (read + write)", file=sys.stderr, flush=True)
+    mc = mfma_ceiling(dev)
+    print(f"[bench] sustained bf16 MFMA on random operands: {mc['TFLOPs']:.0f} TFLOP/s at "
+          f"{mc['clock_GHz']:.2f} GHz", file=sys.stderr, flush=True)
 
     p, d, s = res["mqa_prefill"], res["mqa_decode"], res["sparse_topk"]
     traffic = committed_traffic("mqa_prefill")
@@ -670,6 +746,10 @@ def main():
                    "us_per_call_warm": round(d["ms_warm"] * 1e3, 2),
                    "algorithmic_bytes": d["bytes"], "workload": d["workload"],
                    "hbm_copy_GBps": round(copy_gbps, 1),
+                   "read_floor_us": round(d["read_floor_ms"] * 1e3, 2),
+                   "read_floor_us_warm": round(d["read_floor_ms_warm"] * 1e3, 2),
+                   "read_floor_GBps": round(d["read_floor_gbps"], 1),
+                   "read_floor_over_call": round(d["read_floor_ms"] / d["ms"], 4),
                    "traffic": committed_traffic("mqa_decode")},
         "sparse_topk": {"value": round(s["tflops"], 2), "unit": "TFLOP/s",
                         "frac_of_mfma_peak": round(s["tflops"] / PEAK_BF16_TFLOPS, 4),
@@ -677,6 +757,7 @@ def main():
                         "gather_floor_us": round(s["floor_ms"] * 1e3, 2),
                         "gather_floor_us_warm": round(s["floor_ms_warm"] * 1e3, 2),
                         "gather_floor_GBps": round(s["floor_gbps"], 1),
+                        "gather_floor_over_call": round(s["floor_ms"] / s["ms"], 4),
                         "us_per_call": round(s["ms"] * 1e3, 2),
                         "us_median": round(s["ms_median"] * 1e3, 2),
                         "us_p10": round(s["ms_p10"] * 1e3, 2), "us_p90": round(s["ms_p90"] * 1e3, 2),
@@ -688,6 +769,9 @@ def main():
                            "us_p10": round(p["ms_p10"] * 1e3, 2),
                            "us_p90": round(p["ms_p90"] * 1e3, 2),
                            "us_per_call_warm": round(p["ms_warm"] * 1e3, 2),
+                           "mfma_ceiling_TFLOPs": round(mc["TFLOPs"], 1),
+                           "mfma_ceiling_clock_GHz": round(mc["clock_GHz"], 3),
+                           "frac_of_mfma_ceiling": round(p["tflops"] / mc["TFLOPs"], 4),
                            **committed_kernel_stats("mqa_prefill")},
     }
     line["next"] = nxt

@@ -47,6 +47,9 @@ SIGNATURES = {
     "fmha_topk_select": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p]),
     "fmha_gather_floor": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                    _c_int, _c_int, _c_int, _c_void_p]),
+    "fmha_read_floor": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                 _c_int, _c_int, _c_int, _c_int, _c_void_p]),
+    "fmha_mfma_ceiling": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_void_p]),
     "fmha_status_string": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -446,6 +449,56 @@ def gather_floor(k: torch.Tensor, v: torch.Tensor, kv_idx: torch.Tensor,
     if st != 0:
         raise FmhaError("fmha_gather_floor", st)
     return out
+
+
+def read_floor(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_splits: int,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fmha_read_floor (a measurement helper): the split-KV whole-chunk
+    kernel's reads of q [B, T, n_h, hd] and dense k, v [B, s_k, hd] with no
+    arithmetic; returns one XOR word per workgroup (int32 bit patterns, in
+    launch order tile + tiles * (b + B * split))."""
+    if q.dim() != 4 or k.dim() != 3 or v.shape != k.shape or k.shape[0] != q.shape[0] \
+            or k.shape[2] != q.shape[3]:
+        raise ValueError("q must be [B, T, n_h, hd] and k, v [B, s_k, hd]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous bfloat16")
+    B, T, n_h, hd = q.shape
+    s_k = k.shape[1]
+    n_wg = -(-(T * n_h) // 128) * B * int(num_splits)
+    _same_gpu(q.device, k=k, v=v, out=out)
+    if out is not None:
+        _check_buf("out", out, (n_wg,), (torch.int32,))
+    else:
+        out = torch.empty((n_wg,), dtype=torch.int32, device=q.device)
+    st = _lib.fmha_read_floor(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, n_h, s_k, hd,
+                              int(num_splits), _stream_handle(stream))
+    if st != 0:
+        raise FmhaError("fmha_read_floor", st)
+    return out
+
+
+def mfma_ceiling(ops: torch.Tensor, n_wg: int, iters: int,
+                 sums: Optional[torch.Tensor] = None, clocks: Optional[torch.Tensor] = None,
+                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fmha_mfma_ceiling (a measurement helper): ops bf16 [8, 8, 64, 8] operand
+    fragments; returns (sums fp32 [n_wg, 8, 4], clocks int64 [n_wg, 2]: shader
+    cycles and 100 MHz ticks of each workgroup's loop)."""
+    if ops.dtype != torch.bfloat16 or tuple(ops.shape) != (8, 8, 64, 8) or not ops.is_contiguous():
+        raise ValueError("ops must be a contiguous bfloat16 [8, 8, 64, 8] tensor")
+    dev = ops.device
+    _same_gpu(dev, sums=sums, clocks=clocks)
+    if sums is None:
+        sums = torch.empty((n_wg, 8, 4), dtype=torch.float32, device=dev)
+    if clocks is None:
+        clocks = torch.empty((n_wg, 2), dtype=torch.int64, device=dev)
+    _check_buf("sums", sums, (n_wg, 8, 4), (torch.float32,))
+    _check_buf("clocks", clocks, (n_wg, 2), (torch.int64,))
+    st = _lib.fmha_mfma_ceiling(_ptr(ops), _ptr(sums), _ptr(clocks), int(n_wg), int(iters),
+                                _stream_handle(stream))
+    if st != 0:
+        raise FmhaError("fmha_mfma_ceiling", st)
+    return sums, clocks
 
 
 def raw_fwd(*args) -> int:

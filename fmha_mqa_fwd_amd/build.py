@@ -24,7 +24,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libfmha_mqa.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["api.hip", "fmha_fwd.hip", "fmha_chunk.hip", "lse_merge.hip", "fmha_indexer.hip",
-           "gather_floor.hip", "fmha_hd512.hip"]
+           "gather_floor.hip", "fmha_hd512.hip", "measure.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are kept out of the generated code on purpose; the

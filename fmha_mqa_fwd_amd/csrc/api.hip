@@ -278,6 +278,39 @@ int fmha_gather_floor(const void* k, const void* v, const int32_t* kv_idx, uint3
       s_k, hd, pool_rows, static_cast<hipStream_t>(stream)));
 }
 
+int fmha_read_floor(const void* q, const void* k, const void* v, uint32_t* out, int B, int T,
+                    int n_h, int s_k, int hd, int num_splits, void* stream) {
+  if (B < 0 || T < 0 || n_h < 0 || s_k < 1 || num_splits < 1 || num_splits > s_k)
+    return FMHA_ERR_INVALID_ARG;
+  if (hd != 64 && hd != 128 && hd != 256) return FMHA_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)B * T * n_h;
+  if (rows == 0) return FMHA_OK;
+  const int chunk = (s_k + num_splits - 1) / num_splits;
+  if (chunk > fmha::read_floor_max_keys(hd) || (int64_t)T * n_h > INT32_MAX ||
+      (int64_t)s_k * hd * 2 > INT32_MAX)
+    return FMHA_ERR_UNSUPPORTED;
+  const int64_t grid = ((int64_t)T * n_h + 127) / 128 * B * num_splits;
+  if (grid > INT32_MAX) return FMHA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out) return FMHA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4))
+    return FMHA_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return launch_status(fmha::launch_read_floor(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), out, hd, T * n_h, B, s_k, num_splits,
+      static_cast<hipStream_t>(stream)));
+}
+
+int fmha_mfma_ceiling(const void* ops, float* sums, uint64_t* clocks, int n_wg, int iters,
+                      void* stream) {
+  if (n_wg < 1 || iters < 1) return FMHA_ERR_INVALID_ARG;
+  if (!ops || !sums || !clocks) return FMHA_ERR_INVALID_ARG;
+  if (!aligned(ops, 16) || !aligned(sums, 4) || !aligned(clocks, 8)) return FMHA_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return launch_status(fmha::launch_mfma_ceiling(ops, sums, clocks, n_wg, iters,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int fmha_lse_merge(const float* o_parts, const float* lse_parts, int n_parts, int rows, int hd,
                    void* out, int out_dtype, float* lse, void* stream) {
   if (out_dtype != FMHA_F32 && out_dtype != FMHA_BF16) return FMHA_ERR_INVALID_ARG;

@@ -88,5 +88,14 @@ hipError_t launch_gather_floor(const uint16_t* k, const uint16_t* v, const int32
                                hipStream_t stream);
 hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int P, int top_k,
                        hipStream_t stream);
+// measure.hip: the whole-chunk kernel's reads with no arithmetic (dense
+// groups of rows_per_group rows; chunk of ceil(s_k / num_splits) keys, at most
+// read_floor_max_keys(hd)), and the sustained bf16 MFMA rate
+int read_floor_max_keys(int hd);
+hipError_t launch_read_floor(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             uint32_t* out, int hd, int rows_per_group, int n_groups, int s_k,
+                             int num_splits, hipStream_t stream);
+hipError_t launch_mfma_ceiling(const void* ops, float* sums, uint64_t* clocks, int n_wg,
+                               int iters, hipStream_t stream);
 
 }  // namespace fmha

@@ -171,6 +171,37 @@ int fmha_attention_sink(void* out, float* lse, const float* sink, int rows,
 int fmha_gather_floor(const void* k, const void* v, const int32_t* kv_idx, uint32_t* out,
                       int B, int T, int s_k, int hd, int pool_rows, void* stream);
 
+/* Measurement helper, not part of the attention: the read floor of the
+ * split-KV forward at the decode shape (dense keys, splits that fit LDS
+ * whole).  The same workgroups as the forward's whole-chunk kernel — one per
+ * 128-row tile of a batch's T*n_h rows, per batch and per split — each read
+ * their rows of q (16-byte loads) and their split's K and V rows (LDS-DMA,
+ * all issued at once), with no arithmetic.  out[w], one uint32 per workgroup
+ * w = tile + tiles * (b + B * split), tiles = ceil(T*n_h/128), receives the
+ * XOR of every 32-bit word workgroup w read (so no load can be dropped).
+ *  q bf16 [B, T, n_h, hd];  k, v bf16 [B, s_k, hd];  hd in {64, 128, 256};
+ *  1 <= num_splits <= s_k, and a split of ceil(s_k / num_splits) keys must fit
+ *  64 KiB per tensor (else FMHA_ERR_UNSUPPORTED).  q, k, v 16-byte aligned,
+ *  out 4-byte. */
+int fmha_read_floor(const void* q, const void* k, const void* v, uint32_t* out,
+                    int B, int T, int n_h, int s_k, int hd, int num_splits, void* stream);
+
+/* Measurement helper, not part of the attention: the sustained rate of the
+ * bf16 matrix instruction the attention kernels use (v_mfma_f32_32x32x16_bf16)
+ * on given operands.  n_wg workgroups of 512 threads (eight waves; two per SIMD
+ * once the chip is full) each run, per wave, `iters` rounds of four
+ * independent chains D_c = A_c . B_c + D_c (c = 0..3, D_c starting at 0).
+ *  ops     bf16 [8 waves][8 fragments][64 lanes][8]: fragment 2c is A_c,
+ *          2c+1 is B_c, in the instruction's operand layout (lane l holds row
+ *          or column l % 32 and k = 8 (l / 32) .. +7); shared by every
+ *          workgroup: 65536 bytes, 16-byte aligned
+ *  sums    fp32 [n_wg][8][4]: the sum of all 1024 elements of each final D_c
+ *  clocks  uint64 [n_wg][2]: shader-clock cycles and 100 MHz real-time ticks
+ *          wave 0 of the workgroup spent in its loop (8-byte aligned)
+ * Work per launch: n_wg * 8 * 4 * iters * 32768 FLOP.  n_wg, iters >= 1. */
+int fmha_mfma_ceiling(const void* ops, float* sums, uint64_t* clocks, int n_wg, int iters,
+                      void* stream);
+
 /* Log-sum-exp merge of normalised partial results (page "CURRENT ISSUE: UMMA
  * FMHA — Full Pipeline + Production", "Next steps" 4):
  *   M = max_i lse_i,  w_i = exp(lse_i - M),

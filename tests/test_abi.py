@@ -32,10 +32,11 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["fmha_attention_sink", "fmha_gather_floor",
-                                     "fmha_index_scores", "fmha_lse_merge", "fmha_mqa_fwd",
+                                     "fmha_index_scores", "fmha_lse_merge",
+                                     "fmha_mfma_ceiling", "fmha_mqa_fwd",
                                      "fmha_mqa_fwd_noalloc", "fmha_mqa_fwd_partials",
-                                     "fmha_mqa_fwd_sink",
-                                     "fmha_mqa_workspace_bytes", "fmha_status_string",
+                                     "fmha_mqa_fwd_sink", "fmha_mqa_workspace_bytes",
+                                     "fmha_read_floor", "fmha_status_string",
                                      "fmha_topk_select"]
 
 
@@ -318,3 +319,28 @@ def test_partials_validates_before_launch(F, kw, status):
     """fmha_mqa_fwd_partials rejects bad arguments with the documented status
     (no device is touched: every pointer here is a fake address)."""
     assert _partials(F, **kw) == status
+
+
+@fake_pointers
+@pytest.mark.parametrize("args,status", [
+    ((A, A, A, A, 1, 1, 8, 128, 256, 0, None), 1),       # no splits
+    ((A, A, A, A, 1, 1, 8, 128, 256, 129, None), 1),     # more splits than keys
+    ((A, A, A, A, 1, 1, 8, 0, 256, 1, None), 1),         # no keys
+    ((A, A, A, A, 1, 1, 8, 1024, 512, 8, None), 2),      # head dim
+    ((A, A, A, A, 1, 1, 8, 1024, 256, 4, None), 2),      # 256-key split: over 64 KiB per tensor
+    ((None, A, A, A, 1, 1, 8, 128, 256, 1, None), 1),
+    ((A + 8, A, A, A, 1, 1, 8, 128, 256, 1, None), 3),
+    ((A, A, A, A + 2, 1, 1, 8, 128, 256, 1, None), 3),
+    ((None, None, None, None, 0, 1, 8, 128, 256, 1, None), 0),  # no rows: no-op
+])
+def test_read_floor_validates(F, args, status):
+    assert F._binding._lib.fmha_read_floor(*args) == status
+
+
+@fake_pointers
+@pytest.mark.parametrize("args,status", [
+    ((A, A, A, 0, 10, None), 1), ((A, A, A, 4, 0, None), 1), ((None, A, A, 4, 10, None), 1),
+    ((A + 8, A, A, 4, 10, None), 3), ((A, A, A + 4, 4, 10, None), 3),
+])
+def test_mfma_ceiling_validates(F, args, status):
+    assert F._binding._lib.fmha_mfma_ceiling(*args) == status
