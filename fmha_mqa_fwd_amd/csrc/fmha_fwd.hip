@@ -302,15 +302,15 @@ void fwd_kernel(FwdParams p) {
     if (t + 1 < n_tiles) step(t + 1, sK1, sV1, sK0, sV0, 1);
   }
 
-  // Epilogue through LDS when this workgroup's output rows fit in the K tile
-  // buffers (bf16 outputs), else each lane stores its own pieces.  The last
-  // barrier of the loop has retired every read of those buffers.
+  // Epilogue through LDS for bf16 outputs: each wave stages its 32 rows in a
+  // tile buffer of its own (sK0, sK1, sV0, sV1), so that memory sees whole
+  // 16-byte-per-lane row segments; otherwise each lane stores its own pieces.
+  // The last barrier of the loop has retired every read of those buffers.
   constexpr int RB_BF16 = HDW * 2;
-  constexpr int STAGE_BYTES = NKI * 1024;
   static_assert(QW == 32, "epilogue staging assumes 32 rows per wave");
-  if constexpr (WAVES == 4 && 2 * QW * RB_BF16 <= STAGE_BYTES) {
+  if constexpr (WAVES == 4 && QW * RB_BF16 <= NKI * 1024) {
     if (is_bf16(p.out_mode)) {
-      char* const region = (wave < 2 ? sK0 : sK1) + (wave & 1) * QW * RB_BF16;
+      char* const region = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1;
       w.store_lds(p, grow0, row0, split, lane, [&](int r) { return region + r * RB_BF16; }, col0,
                   dh == 0);
       return;
