@@ -90,7 +90,8 @@ def committed_kernel_stats(workload: str):
     out = {}
     for k, v in rec.get("kernels", {}).items():
         if sig(k) and "merge_kernel" not in k:
-            for key in ("effective_clock_GHz", "mfma_busy_frac"):
+            for key in ("effective_clock_GHz", "mfma_busy_frac", "lds_busy_frac",
+                        "lds_bank_conflict_frac", "valu_active_frac", "mfma_valu_coexec_frac"):
                 if key in v:
                     out[key] = v[key]
     return out
@@ -431,12 +432,60 @@ def _busy_counters(d):
     return res
 
 
-def ingest_counters(fetch_dir, write_dir, busy_dir=None):
+N_CU = 256         # compute units
+
+
+def _pipe_counters(d):
+    """Per fmha kernel (median dispatch), from a run of GRBM_GUI_ACTIVE,
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_VALU_MFMA_COEXEC_CYCLES, SQ_LDS_IDX_ACTIVE,
+    SQ_LDS_BANK_CONFLICT, SQ_ACTIVE_INST_VALU, SQ_INSTS_LDS, SQ_INSTS_VALU:
+    the share of CU cycles the LDS is busy with indexed accesses and the
+    share of those stalled by bank conflicts; the SIMD cycles with vector
+    instructions active (SQ_ACTIVE_INST_VALU counts quad-cycles); the share of
+    matrix-busy cycles in which vector instructions execute too; LDS and
+    vector instructions per dispatch."""
+    by = {}
+    for kname, cn, val, disp, _ in _counter_rows(d):
+        if "fmha" in kname:
+            by.setdefault(kname, {}).setdefault(disp, {})[cn] = val
+    res = {}
+    for k, disps in by.items():
+        cols = {}
+        for c in disps.values():
+            g = c.get("GRBM_GUI_ACTIVE")
+            if not g:
+                continue
+            cyc = g / N_XCD
+            if "SQ_LDS_IDX_ACTIVE" in c:
+                cols.setdefault("lds_busy_frac", []).append(c["SQ_LDS_IDX_ACTIVE"] / (N_CU * cyc))
+                if c["SQ_LDS_IDX_ACTIVE"]:
+                    cols.setdefault("lds_bank_conflict_frac", []).append(
+                        c.get("SQ_LDS_BANK_CONFLICT", 0.0) / c["SQ_LDS_IDX_ACTIVE"])
+            if "SQ_ACTIVE_INST_VALU" in c:
+                cols.setdefault("valu_active_frac", []).append(
+                    4 * c["SQ_ACTIVE_INST_VALU"] / (N_SIMD * cyc))
+            if c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+                cols.setdefault("mfma_busy_frac", []).append(
+                    c["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cyc))
+                if "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
+                    cols.setdefault("mfma_valu_coexec_frac", []).append(
+                        c["SQ_VALU_MFMA_COEXEC_CYCLES"] / c["SQ_VALU_MFMA_BUSY_CYCLES"])
+            for key, cn in (("lds_insts", "SQ_INSTS_LDS"), ("valu_insts", "SQ_INSTS_VALU")):
+                if cn in c:
+                    cols.setdefault(key, []).append(c[cn])
+        if cols:
+            res[k] = {key: round(sorted(v)[len(v) // 2], 4 if "frac" in key else 0)
+                      for key, v in cols.items()}
+    return res
+
+
+def ingest_counters(fetch_dir, write_dir, busy_dir=None, pipe_dir=None):
     """Per-launch HBM bytes of each attention kernel from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
     for a plain copy of COPY_BYTES (expected COPY_BYTES/1024 KiB each way);
     with busy_dir (a GRBM_GUI_ACTIVE + SQ_VALU_MFMA_BUSY_CYCLES run), also the
-    effective clock and matrix-unit busy share of each kernel."""
+    effective clock and matrix-unit busy share of each kernel; with pipe_dir
+    (see _pipe_counters), the LDS, vector and co-execution shares."""
     rec = {"kernel_source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES,
            "workloads": {}, "kernels": {}}
     scale = {}
@@ -464,6 +513,10 @@ def ingest_counters(fetch_dir, write_dir, busy_dir=None):
     rec["copy_scale"] = scale
     if busy_dir:
         for k, b in _busy_counters(busy_dir).items():
+            rec["kernels"].setdefault(k, {}).update(b)
+    if pipe_dir:
+        for k, b in _pipe_counters(pipe_dir).items():
+            b.pop("mfma_busy_frac", None)   # the busy run's figure stays the reported one
             rec["kernels"].setdefault(k, {}).update(b)
     # map kernels to workloads: the attention kernel with the largest traffic
     # of each workload's run is recorded by its template signature
@@ -578,16 +631,18 @@ def main():
                     help="print per-kernel durations (all / flushed calls) of a "
                          "rocprofv3 --kernel-trace run of bench.py")
     ap.add_argument("--ingest-counters", nargs="+", metavar="DIR",
-                    help="FETCH_DIR WRITE_DIR [BUSY_DIR]: turn rocprofv3 --pmc runs "
-                         "(FETCH_SIZE; WRITE_SIZE; GRBM_GUI_ACTIVE + SQ_VALU_MFMA_BUSY_CYCLES) "
-                         "of --only ... --copy-calibration into " + TRAFFIC_FILE)
+                    help="FETCH_DIR WRITE_DIR [BUSY_DIR [PIPE_DIR]]: turn rocprofv3 --pmc "
+                         "runs (FETCH_SIZE; WRITE_SIZE; GRBM_GUI_ACTIVE + "
+                         "SQ_VALU_MFMA_BUSY_CYCLES; the LDS/vector/co-execution counters of "
+                         "_pipe_counters) of --only ... --copy-calibration into "
+                         + TRAFFIC_FILE)
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
         return
     if args.ingest_counters:
-        if len(args.ingest_counters) not in (2, 3):
-            ap.error("--ingest-counters takes FETCH_DIR WRITE_DIR [BUSY_DIR]")
+        if len(args.ingest_counters) not in (2, 3, 4):
+            ap.error("--ingest-counters takes FETCH_DIR WRITE_DIR [BUSY_DIR [PIPE_DIR]]")
         ingest_counters(*args.ingest_counters)
         return
     if args.gpus != 1:

@@ -116,3 +116,29 @@ def test_the_hash_covers_every_library_source():
         assert src in hashed, src
     for hdr in ("fmha_device.h", "fmha_internal.h", "api.hip"):
         assert hdr in hashed, hdr
+
+
+def test_pipe_counters_give_lds_vector_and_coexec_shares(tmp_path):
+    """The LDS / vector / co-execution shares of a kernel from one counter
+    run: per-XCD cycles are GRBM_GUI_ACTIVE / 8; LDS busy per CU cycle,
+    vector-active quad-cycles x 4 per SIMD cycle, co-execution per matrix-busy
+    cycle."""
+    d = tmp_path / "pipe"
+    d.mkdir()
+    cyc = 1000.0
+    vals = {"GRBM_GUI_ACTIVE": cyc * 8, "SQ_LDS_IDX_ACTIVE": 0.25 * 256 * cyc,
+            "SQ_LDS_BANK_CONFLICT": 0.01 * 256 * cyc, "SQ_ACTIVE_INST_VALU": 0.5 * 1024 * cyc / 4,
+            "SQ_VALU_MFMA_BUSY_CYCLES": 0.6 * 1024 * cyc,
+            "SQ_VALU_MFMA_COEXEC_CYCLES": 0.3 * 0.6 * 1024 * cyc,
+            "SQ_INSTS_LDS": 123.0, "SQ_INSTS_VALU": 456.0}
+    rows = [{"Kernel_Name": FWD, "Counter_Name": c, "Counter_Value": v, "Dispatch_Id": 1}
+            for c, v in vals.items()]
+    _write_csv(d / "p_counter_collection.csv",
+               ["Kernel_Name", "Counter_Name", "Counter_Value", "Dispatch_Id"], rows)
+    r = bench._pipe_counters(str(d))[FWD]
+    assert r["lds_busy_frac"] == pytest.approx(0.25)
+    assert r["lds_bank_conflict_frac"] == pytest.approx(0.04)
+    assert r["valu_active_frac"] == pytest.approx(0.5)
+    assert r["mfma_busy_frac"] == pytest.approx(0.6)
+    assert r["mfma_valu_coexec_frac"] == pytest.approx(0.3)
+    assert r["lds_insts"] == 123 and r["valu_insts"] == 456
