@@ -208,7 +208,7 @@ class SourcesCase:
     runs), with every launch's arguments marshalled once."""
 
     def __init__(self, dev, B=32, n_h=64, hd=512, top_k=512, pool=32768, window=128,
-                 splits=(8, 4)):
+                 splits=(4, 2)):
         import fmha_mqa_fwd_amd as F
 
         top = W.make_custom(B=B, T=1, n_h=n_h, hd=hd, s_k=top_k, pool=pool, out_dtype="bf16",
@@ -727,7 +727,7 @@ def main():
     nxt = {}
     nxt_cases = (
         ("hd512_decode", lambda: Case(W.make_custom(B=32, T=1, n_h=128, hd=512, s_k=1024,
-                                                    out_dtype="bf16", num_splits=8, seed=2001,
+                                                    out_dtype="bf16", num_splits=4, seed=2001,
                                                     name="hd512_decode"), dev)),
         ("hd512_flash_topk", lambda: Case(W.make_custom(B=4, T=512, n_h=64, hd=512, s_k=512,
                                                         pool=32768, out_dtype="bf16", seed=2002,

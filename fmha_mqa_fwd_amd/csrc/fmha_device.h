@@ -57,6 +57,38 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* s) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// Workgroup id -> (row tile, group, split).  The dispatcher hands workgroup
+// i to XCD i mod 8, and each XCD has its own L2.  The row tiles of one
+// (group, split) unit read the same K/V, so when a unit has a few of them
+// (at most 8) they are placed 8 ids apart -- same XCD, same dispatch round --
+// and the second reader finds the unit's K/V in that L2.  Units are taken in
+// blocks of 8; a last partial block of rem units is laid out tile-major.
+// With more than 8 row tiles a unit covers every XCD anyway, and its tiles
+// stay consecutive.  A bijection onto [0, tiles) x [0, n_groups * splits).
+struct WgCoords {
+  int tile, group, split;
+};
+__device__ __forceinline__ WgCoords wg_coords(int bid, int tiles, int n_groups) {
+  int tile, unit;
+  if (tiles == 1 || tiles > 8) {
+    tile = bid % tiles;
+    unit = bid / tiles;
+  } else {
+    const int units = (int)(gridDim.x / (unsigned)tiles);
+    const int full = units & ~7;
+    if (bid < full * tiles) {
+      const int blk = bid / (8 * tiles), r = bid - blk * 8 * tiles;
+      tile = r >> 3;
+      unit = blk * 8 + (r & 7);
+    } else {
+      const int r = bid - full * tiles, rem = units - full;
+      tile = r / rem;
+      unit = full + r % rem;
+    }
+  }
+  return {tile, unit % n_groups, unit / n_groups};
+}
+
 // Value of lane l^32 combined with this lane's: max and sum across the halves.
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -63,11 +63,8 @@ void fwd512_kernel(FwdParams p) {
   const int dh = wave & 1;                  // which head-dim half this wave holds
   const int col0 = dh * HDW;
 
-  int bid = blockIdx.x;
-  const int tile = bid % p.tiles_per_group;
-  bid /= p.tiles_per_group;
-  const int group = bid % p.n_groups;
-  const int split = bid / p.n_groups;
+  const WgCoords wc = wg_coords(blockIdx.x, p.tiles_per_group, p.n_groups);
+  const int tile = wc.tile, group = wc.group, split = wc.split;
 
   const int key_lo = split * p.chunk;
   const int key_hi = min(key_lo + p.chunk, p.s_k);

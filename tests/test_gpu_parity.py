@@ -492,11 +492,14 @@ def test_hd512_flash_sparse_topk(F):
     _case(F, w)
 
 
-def test_hd512_decode_benchmarked_size_all_rows(F):
-    """The hd 512 decode row as bench.py times it: B=32, 128 heads, s_k=1024,
-    8 splits, bf16 out, every row."""
-    w = W.make_custom(B=32, T=1, n_h=128, hd=512, s_k=1024, out_dtype="bf16", num_splits=8,
-                      seed=515)
+@pytest.mark.parametrize("splits", [4, 8])
+def test_hd512_decode_benchmarked_size_all_rows(F, splits):
+    """The hd 512 decode row at full size: B=32, 128 heads, s_k=1024, bf16
+    out, every row; bench.py times it with 4 splits (one 256-workgroup launch
+    whose two 64-row tiles of a split share an XCD), 8 is the split count of
+    the hd 256 decode config."""
+    w = W.make_custom(B=32, T=1, n_h=128, hd=512, s_k=1024, out_dtype="bf16",
+                      num_splits=splits, seed=515 + splits)
     _case(F, w)
 
 

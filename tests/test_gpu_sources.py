@@ -84,13 +84,14 @@ def test_decode_shape_two_sources(F):
     _check(out, lse, q, [top, win], scale)
 
 
-def test_two_sources_benchmarked_size_all_rows(F):
-    """The multi-source row as bench.py times it: B=32, 64 heads, hd 512,
-    top-k 512 of a 32768-row pool (8 splits) plus a 128-key window (4 splits),
-    bf16 out; every row against the one-softmax oracle."""
+@pytest.mark.parametrize("splits", [(4, 2), (8, 4)])
+def test_two_sources_benchmarked_size_all_rows(F, splits):
+    """The multi-source row at full size: B=32, 64 heads, hd 512, top-k 512
+    of a 32768-row pool plus a 128-key window, bf16 out, every row against
+    the one-softmax oracle; bench.py times it with (4, 2) splits."""
     q, top, win, scale = _inputs(B=32, T=1, n_h=64, hd=512, pool=32768, top_k=512, window=128,
-                                 seed=98)
-    out, lse = F.fwd_sources(q.to(DEV), [_d(top, 8), _d(win, 4)], scale=scale,
+                                 seed=98 + splits[0])
+    out, lse = F.fwd_sources(q.to(DEV), [_d(top, splits[0]), _d(win, splits[1])], scale=scale,
                              out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     _check(out, lse, q, [top, win], scale)
