@@ -202,13 +202,14 @@ def mfma_ceiling(dev, reps=20):
 
 class SourcesCase:
     """Decode over two key sources — top-k rows gathered from a compressed
-    pool plus a dense sliding window — in one softmax: one forward per source
-    writes its split partials (fmha_mqa_fwd_partials) into planes of one fp32
-    buffer, then one LSE merge over all planes (the composition fwd_sources
-    runs), with every launch's arguments marshalled once."""
+    pool plus a dense sliding window — in one softmax: one
+    fmha_mqa_fwd_sources_partials call writes both sources' split partials
+    into planes of one fp32 buffer (at hd 512, one launch), then one LSE merge
+    over all planes (the composition fwd_sources runs), with every launch's
+    arguments marshalled once."""
 
     def __init__(self, dev, B=32, n_h=64, hd=512, top_k=512, pool=32768, window=128,
-                 splits=(4, 2)):
+                 splits=(4, 1)):
         import fmha_mqa_fwd_amd as F
 
         top = W.make_custom(B=B, T=1, n_h=n_h, hd=hd, s_k=top_k, pool=pool, out_dtype="bf16",
@@ -228,11 +229,9 @@ class SourcesCase:
         # one token per sequence leaves a source's rows few: split its keys so
         # that each launch fills the chip; every split's partial goes to the
         # one merge
-        s0 = splits[0]
-        self.plans = [F.FwdPlan(self.q, kp, vp, idx, scale=top.scale, num_splits=s0,
-                                out=self.parts[:s0], lse=self.lse_parts[:s0], partials=True),
-                      F.FwdPlan(self.q, kw, vw, None, scale=top.scale, num_splits=splits[1],
-                                out=self.parts[s0:], lse=self.lse_parts[s0:], partials=True)]
+        srcs = [(kp, vp, idx, splits[0]), (kw, vw, None, splits[1])]
+        self.plans = [F.SourcesPlan(self.q, srcs, scale=top.scale, o_parts=self.parts,
+                                    lse_parts=self.lse_parts)]
         lib = F._binding._lib
         self._merge = lib.fmha_lse_merge
         self._margs = (self.parts.data_ptr(), self.lse_parts.data_ptr(), n_parts, rows, hd,

@@ -23,6 +23,13 @@ SCRATCH_BYTES = 64 << 20   # FMHA_SCRATCH_BYTES: the static split-KV buffer per 
 
 # Every symbol include/fmha_mqa.h declares, with its ctypes signature.
 _c_int, _c_size, _c_void_p, _c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+class KvSource(ctypes.Structure):
+    """fmha_kv_source: one key source of fmha_mqa_fwd_sources_partials."""
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("kv_idx", ctypes.c_void_p),
+                ("s_k", ctypes.c_int), ("pool_rows", ctypes.c_int),
+                ("num_splits", ctypes.c_int)]
+
+
 SIGNATURES = {
     "fmha_mqa_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "fmha_mqa_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -38,6 +45,9 @@ SIGNATURES = {
     "fmha_mqa_fwd_partials": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                        _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_int, _c_float, _c_int, _c_void_p]),
+    "fmha_mqa_fwd_sources_partials": (_c_int, [_c_void_p, ctypes.POINTER(KvSource), _c_int,
+                                               _c_void_p, _c_void_p, _c_int, _c_int, _c_int,
+                                               _c_int, _c_float, _c_void_p]),
     "fmha_attention_sink": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int,
                                      _c_int, _c_void_p]),
     "fmha_lse_merge": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
@@ -117,6 +127,32 @@ def _check_buf(name: str, t: torch.Tensor, shape, dtypes) -> None:
                          f"tensor of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
 
 
+def _source_dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 kv_idx: Optional[torch.Tensor]) -> Tuple[int, int]:
+    """(s_k, pool_rows) of one key source for q [B, T, n_h, hd]: dense k, v
+    [B, s_k, hd] (kv_idx None) or pools [P, hd] with kv_idx int32 [B, T, s_k];
+    all bf16 and contiguous."""
+    B, T, _, hd = q.shape
+    if kv_idx is None:
+        if k.dim() != 3 or k.shape[0] != B or k.shape[2] != hd or v.shape != k.shape:
+            raise ValueError("dense k/v must be [B, s_k, hd] with q's B and hd")
+        s_k, pool_rows = k.shape[1], 0
+    else:
+        if k.dim() != 2 or k.shape[1] != hd or v.shape != k.shape:
+            raise ValueError("gather k/v pools must be [P, hd] with q's hd")
+        if kv_idx.dtype != torch.int32 or tuple(kv_idx.shape[:2]) != (B, T) or kv_idx.dim() != 3:
+            raise ValueError("kv_idx must be int32 [B, T, s_k]")
+        s_k, pool_rows = kv_idx.shape[2], k.shape[0]
+        if not kv_idx.is_contiguous():
+            raise ValueError("kv_idx must be contiguous")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    return int(s_k), int(pool_rows)
+
+
 def default_scale(hd: int) -> float:
     """1/sqrt(hd) as the fp32 value the kernel receives."""
     return float(torch.tensor(1.0 / math.sqrt(hd), dtype=torch.float32))
@@ -149,23 +185,7 @@ class FwdPlan:
         if q.dim() != 4:
             raise ValueError("q must be [B, T, n_h, hd]")
         B, T, n_h, hd = q.shape
-        if kv_idx is None:
-            if k.dim() != 3 or k.shape[0] != B or k.shape[2] != hd or v.shape != k.shape:
-                raise ValueError("dense k/v must be [B, s_k, hd] with q's B and hd")
-            s_k, pool_rows = k.shape[1], 0
-        else:
-            if k.dim() != 2 or k.shape[1] != hd or v.shape != k.shape:
-                raise ValueError("gather k/v pools must be [P, hd] with q's hd")
-            if kv_idx.dtype != torch.int32 or tuple(kv_idx.shape[:2]) != (B, T) or kv_idx.dim() != 3:
-                raise ValueError("kv_idx must be int32 [B, T, s_k]")
-            s_k, pool_rows = kv_idx.shape[2], k.shape[0]
-            if not kv_idx.is_contiguous():
-                raise ValueError("kv_idx must be contiguous")
-        for name, t in (("q", q), ("k", k), ("v", v)):
-            if t.dtype != torch.bfloat16:
-                raise ValueError(f"{name} must be bfloat16")
-            if not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
+        s_k, pool_rows = _source_dims(q, k, v, kv_idx)
         if sink is not None:
             if sink.dtype != torch.float32 or sink.shape != (n_h,) or not sink.is_contiguous():
                 raise ValueError("sink must be a contiguous float32 [n_h] tensor")
@@ -280,6 +300,62 @@ def fwd_partials(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    stream=stream, partials=True)()
 
 
+class SourcesPlan:
+    """fmha_mqa_fwd_sources_partials with its arguments checked and marshalled
+    once; calling the plan launches again and returns (o_parts, lse_parts):
+    fp32 [sum of splits, B, T, n_h, hd] and [sum of splits, B, T, n_h], the
+    planes of sources[0] first (allocated when None).
+
+    sources: sequence of (k, v, kv_idx, num_splits) as for `fwd_sources`."""
+
+    def __init__(self, q: torch.Tensor, sources, scale: Optional[float] = None,
+                 o_parts: Optional[torch.Tensor] = None,
+                 lse_parts: Optional[torch.Tensor] = None, stream=None):
+        if q.dim() != 4:
+            raise ValueError("q must be [B, T, n_h, hd]")
+        B, T, n_h, hd = q.shape
+        if len(sources) < 1:
+            raise ValueError("at least one key source is needed")
+        dev = q.device
+        descs, keep = [], [q]
+        for src in sources:
+            k, v, kv_idx = src[0], src[1], src[2]
+            splits = int(src[3]) if len(src) > 3 else 1
+            _same_gpu(dev, k=k, v=v, kv_idx=kv_idx)
+            s_k, pool_rows = _source_dims(q, k, v, kv_idx)
+            descs.append(KvSource(_ptr(k), _ptr(v), _ptr(kv_idx), s_k, pool_rows, splits))
+            keep += [k, v, kv_idx]
+        total = sum(d.num_splits for d in descs)
+        if o_parts is None:
+            o_parts = torch.empty((total, B, T, n_h, hd), dtype=torch.float32, device=dev)
+        if lse_parts is None:
+            lse_parts = torch.empty((total, B, T, n_h), dtype=torch.float32, device=dev)
+        _same_gpu(dev, o_parts=o_parts, lse_parts=lse_parts)
+        _check_buf("o_parts", o_parts, (total, B, T, n_h, hd), (torch.float32,))
+        _check_buf("lse_parts", lse_parts, (total, B, T, n_h), (torch.float32,))
+        self._srcs = (KvSource * len(descs))(*descs)
+        self._keep = tuple(keep)
+        self.o_parts, self.lse_parts = o_parts, lse_parts
+        self._args = (_ptr(q), self._srcs, len(descs), _ptr(o_parts), _ptr(lse_parts), B, T,
+                      n_h, hd, float(default_scale(hd) if scale is None else scale),
+                      _stream_handle(stream))
+
+    def __call__(self) -> Tuple[torch.Tensor, torch.Tensor]:
+        st = _lib.fmha_mqa_fwd_sources_partials(*self._args)
+        if st != 0:
+            raise FmhaError("fmha_mqa_fwd_sources_partials", st)
+        return self.o_parts, self.lse_parts
+
+
+def fwd_sources_partials(q: torch.Tensor, sources, scale: Optional[float] = None,
+                         o_parts: Optional[torch.Tensor] = None,
+                         lse_parts: Optional[torch.Tensor] = None, stream=None
+                         ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fmha_mqa_fwd_sources_partials: every source's split partials in one
+    call (see SourcesPlan)."""
+    return SourcesPlan(q, sources, scale, o_parts, lse_parts, stream)()
+
+
 def fwd_sources(q: torch.Tensor, sources, scale: Optional[float] = None,
                 out_dtype: torch.dtype = torch.bfloat16, sink: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
@@ -289,10 +365,11 @@ def fwd_sources(q: torch.Tensor, sources, scale: Optional[float] = None,
 
     sources: sequence of (k, v, kv_idx, num_splits) — dense k, v [B, S, hd]
     with kv_idx None, or pools [P, hd] with kv_idx [B, T, S]; num_splits as
-    for fwd.  Each source writes its split partials with fmha_mqa_fwd_partials
-    into its own planes of one fp32 buffer, and one fmha_lse_merge combines
-    all planes; the sink (fp32 [n_h]) joins once, after the merge
-    (fmha_attention_sink).  Returns (out [B, T, n_h, hd], lse [B, T, n_h]).
+    for fwd.  One fmha_mqa_fwd_sources_partials call writes every source's
+    split partials into its own planes of one fp32 buffer, and one
+    fmha_lse_merge combines all planes; the sink (fp32 [n_h]) joins once,
+    after the merge (fmha_attention_sink).  Returns (out [B, T, n_h, hd], lse
+    [B, T, n_h]).
     """
     if q.dim() != 4:
         raise ValueError("q must be [B, T, n_h, hd]")
@@ -307,15 +384,8 @@ def fwd_sources(q: torch.Tensor, sources, scale: Optional[float] = None,
     if lse is not None:
         _check_buf("lse", lse, (B, T, n_h), (torch.float32,))
     rows = B * T * n_h
-    splits = [int(src[3]) if len(src) > 3 else 1 for src in sources]
-    total = sum(splits)
-    parts = torch.empty((total, B, T, n_h, hd), dtype=torch.float32, device=dev)
-    lse_parts = torch.empty((total, B, T, n_h), dtype=torch.float32, device=dev)
-    first = 0
-    for src, s in zip(sources, splits):
-        fwd_partials(q, src[0], src[1], src[2], scale, s, o_parts=parts[first:first + s],
-                     lse_parts=lse_parts[first:first + s], stream=stream)
-        first += s
+    parts, lse_parts = fwd_sources_partials(q, sources, scale, stream=stream)
+    total = parts.shape[0]
     if out is None:
         out = torch.empty((B, T, n_h, hd), dtype=out_dtype, device=dev)
     if lse is None:

@@ -219,6 +219,71 @@ int fmha_mqa_fwd_partials(const void* q, const void* k, const void* v, const int
                   FMHA_F32, num_splits, nullptr, 0, stream, nullptr, true);
 }
 
+int fmha_mqa_fwd_sources_partials(const void* q, const fmha_kv_source* sources, int n_sources,
+                                  float* o_parts, float* lse_parts, int B, int T, int n_h,
+                                  int hd, float scale, void* stream) {
+  if (n_sources < 1 || !sources) return FMHA_ERR_INVALID_ARG;
+  // every source is checked before anything is launched
+  bool fused = hd == 512 && n_sources <= fmha::MAX_SOURCES;
+  for (int i = 0; i < n_sources; ++i) {
+    const fmha_kv_source& s = sources[i];
+    const int st = fwd_impl(q, s.k, s.v, s.kv_idx, o_parts, lse_parts, B, T, n_h, s.s_k, hd,
+                            s.pool_rows, scale, FMHA_F32, s.num_splits, nullptr, 0, stream,
+                            nullptr, true, true);
+    if (st != FMHA_OK) return st;
+    const int chunk = (s.s_k + s.num_splits - 1) / s.num_splits;
+    if (chunk > fmha::fwd512_max_keys()) fused = false;
+  }
+  const int64_t rows = (int64_t)B * T * n_h;
+  if (rows == 0) return FMHA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!fused) {
+    // one launch per source, each into its own planes
+    int64_t plane = 0;
+    for (int i = 0; i < n_sources; ++i) {
+      const fmha_kv_source& s = sources[i];
+      const int r = fwd_impl(q, s.k, s.v, s.kv_idx, o_parts + plane * rows * hd,
+                             lse_parts + plane * rows, B, T, n_h, s.s_k, hd, s.pool_rows,
+                             scale, FMHA_F32, s.num_splits, nullptr, 0, stream, nullptr, true);
+      if (r != FMHA_OK) return r;
+      plane += s.num_splits;
+    }
+    return FMHA_OK;
+  }
+  // one launch: each source laid out as its own fmha_mqa_fwd_partials would be
+  fmha::SourcesParams sp{};
+  sp.base.q = static_cast<const uint16_t*>(q);
+  sp.base.out = o_parts;
+  sp.base.lse = lse_parts;
+  sp.base.total_rows = rows;
+  sp.base.out_mode = fmha::OUT_PARTIAL;
+  sp.base.scale_log2 = scale * 1.4426950408889634f;
+  sp.base.n_heads = n_h;
+  sp.n_src = n_sources;
+  int plane = 0;
+  int64_t grid = 0;
+  for (int i = 0; i < n_sources; ++i) {
+    const fmha_kv_source& s = sources[i];
+    const bool gather = s.kv_idx != nullptr;
+    fmha::SourceParams& d = sp.src[i];
+    d.k = static_cast<const uint16_t*>(s.k);
+    d.v = static_cast<const uint16_t*>(s.v);
+    d.kv_idx = (gather && s.s_k > 0) ? s.kv_idx : nullptr;
+    d.s_k = s.s_k;
+    d.pool_rows = gather ? s.pool_rows : 0;
+    d.num_splits = s.num_splits;
+    d.chunk = (s.s_k + s.num_splits - 1) / s.num_splits;
+    d.n_groups = gather ? B * T : B;
+    d.rows_per_group = gather ? n_h : T * n_h;
+    d.plane_begin = plane;
+    plane += s.num_splits;
+    grid += (int64_t)((d.rows_per_group + 63) / 64) * d.n_groups * d.num_splits;
+  }
+  if (grid > INT32_MAX) return FMHA_ERR_UNSUPPORTED;
+  (void)hipGetLastError();  // launch errors below are ours alone
+  return launch_status(fmha::launch_fwd512_sources(sp, st));
+}
+
 int fmha_attention_sink(void* out, float* lse, const float* sink, int rows, int n_h, int hd,
                         int out_dtype, void* stream) {
   if (out_dtype != FMHA_F32 && out_dtype != FMHA_BF16) return FMHA_ERR_INVALID_ARG;

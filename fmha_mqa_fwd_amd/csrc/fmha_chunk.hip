@@ -78,7 +78,8 @@ void chunk_kernel(FwdParams p) {
   const int l32 = lane & 31;
   const int hlf = lane >> 5;
 
-  const WgCoords wc = wg_coords(blockIdx.x, p.tiles_per_group, p.n_groups);
+  const WgCoords wc =
+      wg_coords(blockIdx.x, p.tiles_per_group, p.n_groups, p.n_groups * p.num_splits);
   const int tile = wc.tile, group = wc.group, split = wc.split;
 
   const int key_lo = split * p.chunk;

@@ -68,13 +68,12 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* s) {
 struct WgCoords {
   int tile, group, split;
 };
-__device__ __forceinline__ WgCoords wg_coords(int bid, int tiles, int n_groups) {
+__device__ __forceinline__ WgCoords wg_coords(int bid, int tiles, int n_groups, int units) {
   int tile, unit;
   if (tiles == 1 || tiles > 8) {
     tile = bid % tiles;
     unit = bid / tiles;
   } else {
-    const int units = (int)(gridDim.x / (unsigned)tiles);
     const int full = units & ~7;
     if (bid < full * tiles) {
       const int blk = bid / (8 * tiles), r = bid - blk * 8 * tiles;
@@ -207,7 +206,7 @@ struct Rows {
   template <int NKB>
   __device__ __forceinline__ float exps(const f32x16 (&s)[NKB][NQB], bf16x8 (&pf)[NQB][2 * NKB],
                                         int qb, float c, float m_use) const {
-    float ls0 = 0.f, ls1 = 0.f;
+    float ls0, ls1;  // the sums start at the first pair (no add of 0)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -218,8 +217,13 @@ struct Rows {
           const float a = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][8 * h + 2 * j], c, -m_use));
           const float b = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][8 * h + 2 * j + 1], c, -m_use));
           w[j] = pack_bf16x2(a, b);
-          ls0 += a;
-          ls1 += b;
+          if (kb == 0 && h == 0 && j == 0) {
+            ls0 = a;
+            ls1 = b;
+          } else {
+            ls0 += a;
+            ls1 += b;
+          }
         }
         pf[qb][2 * kb + h] = __builtin_bit_cast(bf16x8, w);
       }

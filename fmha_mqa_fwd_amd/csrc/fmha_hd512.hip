@@ -39,9 +39,12 @@ using namespace dev;
 constexpr int G5_HD = 512;
 constexpr int G5_MAX_KEYS = 1024;  // a split's row offsets held in LDS
 
-template <bool GATHER>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fwd512_kernel(FwdParams p) {
+// One workgroup's work: `p` describes its key source, wc its row tile, group
+// and split within that source; its partial (partial modes) goes to plane
+// `plane`.  gather: the source is a pool read through kv_idx (a constant in
+// the one-source kernels, per workgroup in the several-source one).
+__device__ __forceinline__ void fwd512_body(const FwdParams& p, const bool gather,
+                                            const WgCoords wc, const int plane) {
   constexpr int HD = G5_HD, HDW = HD / 2, QW = 32, KT = 32, WAVES = 4, NKS = KT / 16;
   constexpr int M_WG = 2 * QW;              // two row blocks
   constexpr int ROW = HD * 2;               // bytes per K/V row
@@ -63,7 +66,6 @@ void fwd512_kernel(FwdParams p) {
   const int dh = wave & 1;                  // which head-dim half this wave holds
   const int col0 = dh * HDW;
 
-  const WgCoords wc = wg_coords(blockIdx.x, p.tiles_per_group, p.n_groups);
   const int tile = wc.tile, group = wc.group, split = wc.split;
 
   const int key_lo = split * p.chunk;
@@ -75,15 +77,15 @@ void fwd512_kernel(FwdParams p) {
 
   // gather: the pools; dense: this batch's keys (byte counts fit 32 bits: the
   // host checks rows * hd * 2)
-  const int64_t kv0 = GATHER ? 0 : (int64_t)group * p.s_k * HD;
-  const uint32_t kv_bytes = (uint32_t)(GATHER ? p.pool_rows : p.s_k) * ROW;
+  const int64_t kv0 = gather ? 0 : (int64_t)group * p.s_k * HD;
+  const uint32_t kv_bytes = (uint32_t)(gather ? p.pool_rows : p.s_k) * ROW;
   const u32x4 rk = buffer_rsrc(p.k + kv0, kv_bytes);
   const u32x4 rv = buffer_rsrc(p.v + kv0, kv_bytes);
   const uint32_t lane16 = 16u * (uint32_t)lane;
 
   // the split's row offsets: gather, the index list validated into pool byte
   // offsets; dense, the keys' offsets in this batch's K/V
-  if constexpr (GATHER) {
+  if (gather) {
     const int32_t* ibase = p.kv_idx + (int64_t)group * p.s_k + key_lo;
     for (int i = tid; i < n_tiles * KT; i += 256) {
       int idx = -1;
@@ -210,11 +212,45 @@ void fwd512_kernel(FwdParams p) {
   static_assert(2 * QW * RB_BF16 <= KT * KS, "epilogue staging");
   if (is_bf16(p.out_mode)) {
     char* const region = ((wave >> 1) == 0 ? sK0 : sK1) + dh * QW * RB_BF16;
-    w.store_lds(p, grow0, row0, split, lane, [&](int r) { return region + r * RB_BF16; }, col0,
+    w.store_lds(p, grow0, row0, plane, lane, [&](int r) { return region + r * RB_BF16; }, col0,
                 dh == 0);
     return;
   }
-  w.store(p, grow0, row0, split, l32, hlf, col0, dh == 0);
+  w.store(p, grow0, row0, plane, l32, hlf, col0, dh == 0);
+}
+
+template <bool GATHER>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd512_kernel(FwdParams p) {
+  const WgCoords wc =
+      wg_coords(blockIdx.x, p.tiles_per_group, p.n_groups, p.n_groups * p.num_splits);
+  fwd512_body(p, GATHER, wc, wc.split);
+}
+
+// Several key sources in one launch: workgroup blockIdx.x belongs to the last
+// source whose first workgroup is at or before it, and is placed within that
+// source exactly as a one-source launch would place it.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd512_sources_kernel(SourcesParams sp) {
+  const int bid = blockIdx.x;
+  SourceParams src = sp.src[0];
+#pragma unroll
+  for (int i = 1; i < MAX_SOURCES; ++i)
+    if (i < sp.n_src && bid >= sp.src[i].wg_begin) src = sp.src[i];
+  FwdParams p = sp.base;
+  p.k = src.k;
+  p.v = src.v;
+  p.kv_idx = src.kv_idx;
+  p.s_k = src.s_k;
+  p.pool_rows = src.pool_rows;
+  p.chunk = src.chunk;
+  p.num_splits = src.num_splits;
+  p.n_groups = src.n_groups;
+  p.rows_per_group = src.rows_per_group;
+  p.tiles_per_group = src.tiles_per_group;
+  const WgCoords wc = wg_coords(bid - src.wg_begin, src.tiles_per_group, src.n_groups,
+                                src.n_groups * src.num_splits);
+  fwd512_body(p, src.kv_idx != nullptr, wc, src.plane_begin + wc.split);
 }
 
 }  // namespace
@@ -227,6 +263,21 @@ hipError_t launch_fwd512(const FwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(fwd512_kernel<true>, grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(fwd512_kernel<false>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd512_sources(SourcesParams sp, hipStream_t stream) {
+  if (sp.n_src < 1 || sp.n_src > MAX_SOURCES) return hipErrorInvalidValue;
+  int64_t wg = 0;
+  for (int i = 0; i < sp.n_src; ++i) {
+    SourceParams& s = sp.src[i];
+    if (s.chunk > G5_MAX_KEYS) return hipErrorInvalidValue;
+    s.tiles_per_group = (s.rows_per_group + 63) / 64;  // 64-row tiles
+    s.wg_begin = (int)wg;
+    wg += (int64_t)s.tiles_per_group * s.n_groups * s.num_splits;
+  }
+  if (wg < 1 || wg > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fwd512_sources_kernel, dim3((unsigned)wg), dim3(256), 0, stream, sp);
   return hipGetLastError();
 }
 

@@ -61,6 +61,29 @@ hipError_t launch_chunk(FwdParams p, int hd, hipStream_t stream);
 int fwd512_max_keys();
 hipError_t launch_fwd512(const FwdParams& p, hipStream_t stream);
 
+// Several key sources in one head-dim-512 launch, partial mode: source i's
+// splits write planes plane_begin .. plane_begin + num_splits - 1 of the
+// launch's [sum of splits, total_rows, hd] buffer (base.out / base.lse).
+// Each source is laid out as a one-source launch would be (its groups: a
+// token when it gathers, a batch when dense); launch_fwd512_sources fills in
+// tiles_per_group and wg_begin.  Every source's chunk is at most
+// fwd512_max_keys().
+constexpr int MAX_SOURCES = 4;
+struct SourceParams {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* kv_idx;  // nullptr: dense
+  int s_k, pool_rows, chunk, num_splits, n_groups, rows_per_group, tiles_per_group;
+  int wg_begin;           // first workgroup of this source
+  int plane_begin;        // first partial plane of this source
+};
+struct SourcesParams {
+  FwdParams base;         // q, out, lse, total_rows, out_mode, scale_log2, n_heads
+  int n_src;
+  SourceParams src[MAX_SOURCES];
+};
+hipError_t launch_fwd512_sources(SourcesParams sp, hipStream_t stream);
+
 // out[r] = sum_i w_i o_i[r] / sum_i w_i with w_i = exp(lse_i[r] - max_i lse_i[r]).
 // o_parts holds fp32, or bf16 when parts_bf16.  With sink (optional,
 // [n_heads]), the sink of row r's head r % n_heads joins the merged result

@@ -150,6 +150,43 @@ int fmha_mqa_fwd_partials(const void* q, const void* k, const void* v,
                           int B, int T, int n_h, int s_k, int hd, int pool_rows,
                           float scale, int num_splits, void* stream);
 
+/* One key source of fmha_mqa_fwd_sources_partials: the arguments that
+ * fmha_mqa_fwd_partials takes per call.
+ *  k, v        bf16: dense [B, s_k, hd] (kv_idx NULL), or pools [pool_rows, hd]
+ *  kv_idx      NULL, or int32 [B, T, s_k] pool rows (entries outside
+ *              [0, pool_rows) are masked, as in fmha_mqa_fwd)
+ *  s_k         keys per query row from this source (>= 0)
+ *  pool_rows   gather: rows in the pools (>= 1); dense: ignored
+ *  num_splits  1 .. max(s_k, 1): this source's partial planes */
+typedef struct fmha_kv_source {
+  const void* k;
+  const void* v;
+  const int32_t* kv_idx;
+  int s_k;
+  int pool_rows;
+  int num_splits;
+} fmha_kv_source;
+
+/* The partials of several key sources in one call: the split planes of
+ * sources[0], then those of sources[1], ..., in one buffer, so that one
+ * fmha_lse_merge over all of them gives attention over the union of the
+ * sources' keys (page "May 24, 2026 — Session Start Plan": the top-k rows
+ * gathered from the compressed pool, File Map and Key Numbers; a sliding
+ * window of recent keys beside them is the second source this serves).
+ *  sources    n_sources >= 1 entries, read during the call only
+ *  o_parts    fp32 [sum of num_splits, B*T*n_h, hd], 16-byte aligned
+ *  lse_parts  fp32 [sum of num_splits, B*T*n_h], 4-byte aligned
+ * Every plane is what fmha_mqa_fwd_partials writes for that source and split
+ * (bit for bit).  At hd 512, with at most 4 sources whose splits have at most
+ * 1024 keys each, all sources' splits run in one kernel launch; otherwise one
+ * launch per source.  Every source is validated before anything is enqueued;
+ * errors as fmha_mqa_fwd_partials (FMHA_ERR_INVALID_ARG also for n_sources < 1
+ * or sources NULL). */
+int fmha_mqa_fwd_sources_partials(const void* q, const fmha_kv_source* sources,
+                                  int n_sources, float* o_parts, float* lse_parts,
+                                  int B, int T, int n_h, int hd, float scale,
+                                  void* stream);
+
 /* The same sink applied in place to finished rows (for results already merged
  * from several sources): for r in [0, rows), with h = r % n_h,
  *   lse[r] <- ln(exp(lse[r]) + exp(sink[h])),  out[r, :] *= exp(lse_old - lse_new).

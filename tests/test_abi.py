@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
                                      "fmha_index_scores", "fmha_lse_merge",
                                      "fmha_mfma_ceiling", "fmha_mqa_fwd",
                                      "fmha_mqa_fwd_noalloc", "fmha_mqa_fwd_partials",
-                                     "fmha_mqa_fwd_sink", "fmha_mqa_workspace_bytes",
+                                     "fmha_mqa_fwd_sink", "fmha_mqa_fwd_sources_partials",
+                                     "fmha_mqa_workspace_bytes",
                                      "fmha_read_floor", "fmha_status_string",
                                      "fmha_topk_select"]
 
@@ -319,6 +320,46 @@ def test_partials_validates_before_launch(F, kw, status):
     """fmha_mqa_fwd_partials rejects bad arguments with the documented status
     (no device is touched: every pointer here is a fake address)."""
     assert _partials(F, **kw) == status
+
+
+def _sources(F, srcs, **kw):
+    """fmha_mqa_fwd_sources_partials over (k, v, kv_idx, s_k, pool_rows,
+    num_splits) tuples; srcs None passes a NULL source array."""
+    args = dict(q=A, o=A, l=A, B=1, T=1, n_h=1, hd=512, scale=0.125, stream=None, n=None)
+    args.update(kw)
+    arr = None
+    if srcs is not None:
+        arr = (F.KvSource * max(len(srcs), 1))(*[F.KvSource(*x) for x in srcs])
+    n = len(srcs or []) if args["n"] is None else args["n"]
+    return F._binding._lib.fmha_mqa_fwd_sources_partials(
+        args["q"], arr, n, args["o"], args["l"], args["B"], args["T"], args["n_h"], args["hd"],
+        args["scale"], args["stream"])
+
+
+TOP = (A, A, A, 8, 100, 2)    # gather source: 8 keys of a 100-row pool, 2 splits
+WIN = (A, A, None, 4, 0, 1)   # dense source: 4 keys
+
+
+@fake_pointers
+@pytest.mark.parametrize("srcs,kw,status", [
+    ([TOP, WIN], dict(B=0), 0),                           # nothing to compute
+    ([], {}, 1),                                          # no sources
+    (None, dict(n=2), 1),                                 # NULL source array
+    ([TOP, WIN], dict(hd=96), 2),
+    ([TOP, (A, A, None, 4, 0, 5)], {}, 1),                # second source: more splits than keys
+    ([(A, A, A, 8, 0, 1), WIN], {}, 1),                   # gather without a pool
+    ([TOP, (None, A, None, 4, 0, 1)], {}, 1),             # second source without k
+    ([TOP, (A + 8, A, None, 4, 0, 1)], {}, 3),            # second source's k misaligned
+    ([TOP, WIN], dict(o=A + 4), 3),
+    ([TOP, WIN], dict(l=A + 2), 3),
+    ([TOP, WIN], dict(scale=0.0), 1),
+    ([TOP, WIN], dict(q=None), 1),
+])
+def test_sources_partials_validate_every_source_before_launch(F, srcs, kw, status):
+    """fmha_mqa_fwd_sources_partials rejects a bad source (first or later)
+    with fmha_mqa_fwd_partials' status before anything is launched (every
+    pointer here is a fake address)."""
+    assert _sources(F, srcs, **kw) == status
 
 
 @fake_pointers

@@ -1,7 +1,9 @@
 """GPU parity of attention over several key sources (top-k rows gathered from
-a compressed pool + a dense sliding window), composed from fmha_mqa_fwd per
-source, fmha_lse_merge and the sink, against oracle.attention_sources (one
-softmax over the concatenated keys).  Same bar as the plain forward."""
+a compressed pool + a dense sliding window), composed from
+fmha_mqa_fwd_sources_partials (every source's split partials in one call),
+fmha_lse_merge and the sink, against oracle.attention_sources (one softmax
+over the concatenated keys).  Same bar as the plain forward; the one-call
+partials also equal fmha_mqa_fwd_partials per source bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -84,14 +86,82 @@ def test_decode_shape_two_sources(F):
     _check(out, lse, q, [top, win], scale)
 
 
-@pytest.mark.parametrize("splits", [(4, 2), (8, 4)])
+@pytest.mark.parametrize("splits", [(4, 1), (8, 4)])
 def test_two_sources_benchmarked_size_all_rows(F, splits):
     """The multi-source row at full size: B=32, 64 heads, hd 512, top-k 512
     of a 32768-row pool plus a 128-key window, bf16 out, every row against
-    the one-softmax oracle; bench.py times it with (4, 2) splits."""
+    the one-softmax oracle; bench.py times it with (4, 1) splits (every
+    workgroup of the one launch takes 128 keys)."""
     q, top, win, scale = _inputs(B=32, T=1, n_h=64, hd=512, pool=32768, top_k=512, window=128,
                                  seed=98 + splits[0])
     out, lse = F.fwd_sources(q.to(DEV), [_d(top, splits[0]), _d(win, splits[1])], scale=scale,
                              out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     _check(out, lse, q, [top, win], scale)
+
+
+def _top_and_window(B, T, n_h, hd, pool, top_k, window, seed, mask=True):
+    """Inputs as _inputs; with mask, some top-k entries are invalid (outside
+    [0, pool): masked keys)."""
+    q, top, win, scale = _inputs(B=B, T=T, n_h=n_h, hd=hd, pool=pool, top_k=max(top_k, 1),
+                                 window=window, seed=seed)
+    kp, vp, idx = top
+    if top_k == 0:
+        idx = torch.zeros((B, T, 0), dtype=torch.int32)
+    elif mask:
+        idx = idx.clone()
+        idx[0, 0, ::7] = -1           # masked entries: outside [0, pool)
+        idx[-1, -1, 1::5] = pool + 3
+    return q, (kp, vp, idx), win, scale
+
+
+@pytest.mark.parametrize("hd,B,T,n_h,pool,top_k,window,splits", [
+    (512, 2, 1, 64, 4096, 512, 128, (4, 2)),   # one launch, the decode shape
+    (512, 2, 3, 24, 2048, 300, 70, (3, 2)),    # one launch; token groups beside batch groups
+    (512, 1, 2, 8, 512, 0, 40, (1, 1)),        # an empty top-k source
+    (512, 3, 1, 16, 1024, 100, 33, (1, 3)),
+    (128, 2, 3, 16, 2048, 200, 64, (2, 1)),    # one launch per source
+])
+def test_sources_partials_equal_per_source_partials(F, hd, B, T, n_h, pool, top_k, window,
+                                                    splits):
+    """fmha_mqa_fwd_sources_partials writes, plane for plane and bit for bit,
+    what fmha_mqa_fwd_partials writes for each source on its own."""
+    q, top, win, scale = _top_and_window(B, T, n_h, hd, pool, top_k, window, seed=300 + hd + T)
+    qd = q.to(DEV)
+    srcs = [_d(top, splits[0]), _d(win, splits[1])]
+    o, lse = F.fwd_sources_partials(qd, srcs, scale)
+    first = 0
+    for src in srcs:
+        o1, l1 = F.fwd_partials(qd, src[0], src[1], src[2], scale, src[3])
+        torch.cuda.synchronize()
+        s = src[3]
+        assert torch.equal(o[first:first + s], o1), first
+        assert torch.equal(lse[first:first + s], l1), first
+        first += s
+    assert first == o.shape[0]
+
+
+@pytest.mark.parametrize("n_src", [3, 5])
+def test_several_sources_at_hd512(F, n_src):
+    """Three sources run in one launch, five (over the one-launch limit of
+    four) in one launch each; both match the one-softmax oracle over all keys
+    and the per-source partials bit for bit."""
+    q, top, win, scale = _top_and_window(2, 2, 16, 512, 1024, 96, 40, seed=400, mask=False)
+    srcs_h = [top, win]
+    for i in range(n_src - 2):
+        _, t2, _, _ = _top_and_window(2, 2, 16, 512, 700, 50 + 9 * i, 1, seed=410 + i,
+                                      mask=False)
+        srcs_h.append(t2)
+    qd = q.to(DEV)
+    srcs = [_d(s, 1 + (i % 3)) for i, s in enumerate(srcs_h)]
+    o, lse = F.fwd_sources_partials(qd, srcs, scale)
+    first = 0
+    for src in srcs:
+        o1, l1 = F.fwd_partials(qd, src[0], src[1], src[2], scale, src[3])
+        torch.cuda.synchronize()
+        s = src[3]
+        assert torch.equal(o[first:first + s], o1) and torch.equal(lse[first:first + s], l1)
+        first += s
+    out, L = F.fwd_sources(qd, srcs, scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check(out, L, q, srcs_h, scale)
