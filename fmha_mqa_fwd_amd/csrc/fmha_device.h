@@ -285,10 +285,13 @@ struct Rows {
   __device__ __forceinline__ int softmax(f32x16 (&s)[NKB][NQB], bf16x8 (&pf)[NQB][2 * NKB],
                                          float c) {
     float ls[NQB];
-    const bool slow = softmax_fast<NKB>(s, pf, c, ls);
-    if (slow) softmax_slow<NKB>(s, pf, c, ls);
+    if (!softmax_fast<NKB>(s, pf, c, ls)) {
+      commit_l(ls);
+      return 0;
+    }
+    softmax_slow<NKB>(s, pf, c, ls);
     commit_l(ls);
-    return slow;
+    return 1;
   }
 
   __device__ __forceinline__ void rescale_o() {

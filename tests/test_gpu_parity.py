@@ -418,6 +418,33 @@ def test_large_magnitude_logits_stay_finite(F):
     _check(out, lse, q, k, v, None, w.scale)
 
 
+@pytest.mark.parametrize("splits,gather", [(1, False), (4, False), (1, True)])
+def test_large_values_error_bounded_by_the_p_rounding(F, splits, gather):
+    """V ~ N(0, 1000^2), fp32 out: the absolute bar has no meaning at this
+    scale, so the bound is the one the bf16 P operand implies.  Each weight
+    is rounded once, p~ = p (1 + e) with |e| <= 2^-8, so |O - O_ref| <=
+    2^-8 * sum p |v| / sum p per element (plus fp32 accumulation); the oracle
+    gives that weighted mean of |v| as attention over |v|.  The merge of split
+    parts keeps the bound (its weights sum to one).  Per-row cosine and lse
+    keep the usual bar."""
+    w = W.make_custom(B=2, T=3, n_h=40, hd=128, s_k=700, out_dtype="f32", num_splits=splits,
+                      pool=2048 if gather else 0, seed=31 + splits + 10 * gather)
+    q, k, v, idx = W.make_inputs(w)
+    v = (v.float() * 1000).to(torch.bfloat16)
+    out, lse = _run(F, q, k, v, idx, w.scale, torch.float32, splits)
+    O_ref, L_ref = oracle.attention(q, k, v, w.scale, kv_idx=idx)
+    A_ref, _ = oracle.attention(q, k, v.float().abs().to(torch.bfloat16), w.scale, kv_idx=idx)
+    o = out.float().cpu().numpy().astype(np.float64)
+    err = np.abs(o - O_ref)
+    bound = (2.0 ** -8 + 1e-4) * A_ref + 1e-6   # 1e-4: fp32 sums over 700 keys
+    assert np.all(err <= bound), float((err / bound).max())
+    m = oracle.row_metrics(o.reshape(-1, 128), O_ref.reshape(-1, 128), lse.cpu().numpy().ravel(),
+                           L_ref.ravel())
+    assert m["min_row_cos"] >= MIN_COS and m["lse_err"] <= LSE_ERR, m
+    say(f"[parity] |V|~1000 splits={splits} gather={gather}: max err/bound "
+        f"{float((err / bound).max()):.3f}, max_abs {m['max_abs']:.3e}")
+
+
 def test_single_key_returns_that_value_row(F):
     """s_k = 1: O = V_0.  The kernel folds scale*log2(e) into an FMA, so the
     lone weight is 1 within fp32 rounding, not bit-exactly."""
