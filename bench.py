@@ -515,8 +515,10 @@ def ingest_counters(fetch_dir, write_dir, busy_dir=None, pipe_dir=None):
             rec["kernels"].setdefault(k, {}).update(b)
     if pipe_dir:
         for k, b in _pipe_counters(pipe_dir).items():
-            b.pop("mfma_busy_frac", None)   # the busy run's figure stays the reported one
-            rec["kernels"].setdefault(k, {}).update(b)
+            ent = rec["kernels"].setdefault(k, {})
+            if "mfma_busy_frac" in ent:   # the busy run's figure stays the reported one
+                b.pop("mfma_busy_frac", None)
+            ent.update(b)
     # map kernels to workloads: the attention kernel with the largest traffic
     # of each workload's run is recorded by its template signature
     for name, _ in CASES:
