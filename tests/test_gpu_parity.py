@@ -538,6 +538,49 @@ def test_hd512_flash_topk_benchmarked_size_all_rows(F):
     _case(F, w)
 
 
+@pytest.mark.parametrize("T,n_h,s_k,pool,out_dtype,plant", [
+    (600, 64, 512, 4096, "bf16", False),   # 600 workgroups: more than one round on the chip
+    (200, 100, 512, 2048, "bf16", False),  # two row tiles per token, the second of 36 rows
+    (400, 64, 100, 1000, "f32", True),     # four tiles, the last partly past s_k; bad entries
+    (300, 64, 1024, 8192, "bf16", False),  # 32 tiles per token
+])
+def test_hd512_gather_many_tokens(F, T, n_h, s_k, pool, out_dtype, plant):
+    """The head-dim-512 gather over more tokens than the chip runs at once:
+    ragged heads, invalid and repeated entries, a last tile partly past s_k, 32
+    tiles per token.  Every row against the oracle, and the first 200 row tiles
+    bit-equal to a call over those tokens alone (a row's result does not depend
+    on the size of the launch)."""
+    w = W.make_custom(B=1, T=T, n_h=n_h, hd=512, s_k=s_k, pool=pool, out_dtype=out_dtype,
+                      seed=900 + T + s_k)
+    q, k, v, idx = W.make_inputs(w)
+    if plant:
+        idx = idx.clone()
+        idx[0, ::7, 3] = -1            # invalid entries: masked keys
+        idx[0, ::5, 17] = pool         # one past the pool
+        idx[0, ::9, 40] = pool + 1000
+        idx[0, ::3, 50] = idx[0, ::3, 51]  # a row gathered twice
+    dt = _dt(out_dtype)
+    out, lse = _run(F, q, k, v, idx, w.scale, dt, 1)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    # tokens with invalid entries: attention over their valid entries alone
+    bad_t = [t for t in range(T) if ((idx[0, t] < 0) | (idx[0, t] >= pool)).any()]
+    for t in bad_t:
+        ok = [int(j) for j in idx[0, t] if 0 <= int(j) < pool]
+        sub = torch.tensor([[ok]], dtype=torch.int32)
+        _check(out[:, t:t + 1], lse[:, t:t + 1], q[:, t:t + 1], k, v, sub, w.scale)
+    good = sorted(set(range(T)) - set(bad_t))
+    m = _check(out, lse, q, k, v, idx, w.scale,
+               rows=None if not bad_t else [t * n_h + h for t in good for h in range(n_h)])
+    t_small = 200 // ((n_h + 63) // 64)
+    out2, lse2 = _run(F, q[:, :t_small].contiguous(), k, v, idx[:, :t_small].contiguous(),
+                      w.scale, dt, 1)
+    assert torch.equal(out[:, :t_small], out2)
+    assert torch.equal(lse[:, :t_small], lse2)
+    say(f"[parity] hd 512 gather {w.describe()}: max_abs {m['max_abs']:.3e} "
+        f"min_row_cos {m['min_row_cos']:.7f} lse_err {m['lse_err']:.3e}; first {t_small} "
+        f"tokens bit-equal to a call over them alone")
+
+
 @pytest.mark.parametrize("s_k,splits", [(1024, 1), (1025, 1), (2000, 1), (2000, 2)])
 def test_hd512_dense_key_counts_around_the_staged_limit(F, s_k, splits):
     """At head dim 512 a split of up to 1024 keys runs the kernel that stages
