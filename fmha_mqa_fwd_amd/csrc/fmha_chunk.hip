@@ -153,10 +153,13 @@ void chunk_kernel(FwdParams p) {
           offv = (uint32_t)row * ROW + 16 * (phys ^ swz_v<CPR>(row));
         }
         const int lds_off = (wave * IPW + j) * 1024;
+        // dense: each split's K/V is read by its own workgroups only, once
+        // (non-temporal); gathered pool rows are shared between tokens
+        constexpr int CPOL = GATHER ? 0 : CPOL_NT;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void*)(kgrp(g) + lds_off), 16, offk, 0, 0, 0);
+            rk, (__attribute__((address_space(3))) void*)(kgrp(g) + lds_off), 16, offk, 0, 0, CPOL);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)(vgrp(g) + lds_off), 16, offv, 0, 0, 0);
+            rv, (__attribute__((address_space(3))) void*)(vgrp(g) + lds_off), 16, offv, 0, 0, CPOL);
       }
     }
   }

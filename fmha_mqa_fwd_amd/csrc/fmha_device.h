@@ -40,6 +40,9 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr float SUM_LIMIT = 4096.0f;
 // gfx9 raw buffer descriptor word 3 (32-bit data, no swizzle, offset mode)
 constexpr int BUF_FLAGS = 0x00020000;
+// Cache-policy operand of the buffer-load builtins: the non-temporal bit
+// (data read once; measured ~1% faster for the split-KV decode's K/V).
+constexpr int CPOL_NT = 2;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -444,6 +447,14 @@ constexpr uint32_t OOB = 0x80000000u;  // beyond any descriptor's byte count: re
 // wait_vmcnt.  M0 (the LDS destination) is the asm operand bound to m0.
 __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "{m0}"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// The same, non-temporal (data read once).
+__device__ __forceinline__ void dma16_nt(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
                :
                : "{m0}"(lds_addr), "v"(voff), "s"(rsrc)
                : "memory");

@@ -136,7 +136,10 @@ __device__ __forceinline__ void fwd512_body(const FwdParams& p, const bool gathe
       __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < RPW; ++j)
-      dma16(rsrc, (uint32_t)(uintptr_t)(buf + (wave * RPW + j) * stride), o.o[j]);
+      if (gather)  // pool rows are shared between tokens; a split's keys are read once
+        dma16(rsrc, (uint32_t)(uintptr_t)(buf + (wave * RPW + j) * stride), o.o[j]);
+      else
+        dma16_nt(rsrc, (uint32_t)(uintptr_t)(buf + (wave * RPW + j) * stride), o.o[j]);
   };
   auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
