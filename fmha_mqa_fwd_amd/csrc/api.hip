@@ -129,10 +129,14 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* kv_idx,
   p.out_mode = bf16_parts ? fmha::OUT_PARTIAL_BF16 : fmha::OUT_PARTIAL;
   int s = launch_status(fmha::launch_fwd(p, hd, st));
   if (s != FMHA_OK) return s;
-  // the sink joins once, in the merge (the partials carry none)
+  // the sink joins once, in the merge (the partials carry none).  With a
+  // multiple of 8 groups of at most 512 rows (at most 8 row tiles), the
+  // attention kernels' placement put every split and tile of group g on XCD
+  // g mod 8 (wg_coords), and the merge follows it.
+  const int group_rows = (p.n_groups % 8 == 0 && p.rows_per_group <= 512) ? p.rows_per_group : 0;
   return launch_status(fmha::launch_merge(o_part, lse_part, num_splits, (int)rows, hd, out,
                                           out_dtype == FMHA_BF16, lse, st, sink, n_h,
-                                          bf16_parts));
+                                          bf16_parts, group_rows));
 }
 
 constexpr int kMaxDevices = 64;

@@ -87,11 +87,13 @@ hipError_t launch_fwd512_sources(SourcesParams sp, hipStream_t stream);
 // out[r] = sum_i w_i o_i[r] / sum_i w_i with w_i = exp(lse_i[r] - max_i lse_i[r]).
 // o_parts holds fp32, or bf16 when parts_bf16.  With sink (optional,
 // [n_heads]), the sink of row r's head r % n_heads joins the merged result
-// (see sink_adjust in fmha_device.h).
+// (see sink_adjust in fmha_device.h).  group_rows > 0: the parts were written
+// by a launch whose every split and row tile of group g (group_rows rows) ran
+// on XCD g mod 8; the merge then takes each group's rows on that XCD.
 hipError_t launch_merge(const void* o_parts, const float* lse_parts, int n_parts,
                         int rows, int hd, void* out, bool out_bf16, float* lse,
                         hipStream_t stream, const float* sink = nullptr, int n_heads = 1,
-                        bool parts_bf16 = false);
+                        bool parts_bf16 = false, int group_rows = 0);
 
 // In place: out[r] *= exp(lse[r] - lse'[r]), lse'[r] = ln(exp(lse[r]) + exp(sink[r % n_heads])).
 hipError_t launch_sink(void* out, float* lse, const float* sink, int rows, int n_heads, int hd,

@@ -598,6 +598,32 @@ def test_hd512_dense_prefill(F, splits, out_dtype):
 
 
 # --------------------------------------------------------------- the merge
+@pytest.mark.parametrize("B,T,n_h,hd,pool,splits", [
+    (8, 1, 128, 64, 0, 8), (16, 1, 128, 128, 0, 5), (8, 1, 128, 256, 0, 8),
+    (8, 1, 128, 512, 0, 4), (8, 1, 256, 256, 0, 3), (2, 4, 64, 128, 1000, 4),
+    (3, 1, 128, 256, 0, 8), (8, 1, 100, 128, 0, 6)])
+def test_split_path_merge_equals_the_merge_of_its_partials(F, B, T, n_h, hd, pool, splits):
+    """fmha_mqa_fwd with splits (fp32 out: fp32 partials) is, bit for bit, the
+    public merge of fmha_mqa_fwd_partials' planes for the same call.  A multiple
+    of 8 groups with at most 512 rows each takes the merge's XCD-following
+    block order, the other cases its plain order; the arithmetic of a row is
+    the same either way."""
+    w = W.make_custom(B=B, T=T, n_h=n_h, hd=hd, s_k=700, pool=pool, out_dtype="f32",
+                      num_splits=splits, seed=B * 31 + n_h + hd + splits)
+    q, k, v, idx = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    idd = None if idx is None else idx.to(dev)
+    out, lse = F.fwd(qd, kd, vd, idd, scale=w.scale, out_dtype=torch.float32, num_splits=splits)
+    o_parts, l_parts = F.fwd_partials(qd, kd, vd, idd, scale=w.scale, num_splits=splits)
+    rows = B * T * n_h
+    o2, l2 = F.lse_merge(o_parts.view(splits, rows, hd), l_parts.view(splits, rows),
+                         torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(rows, hd), o2) and torch.equal(lse.view(rows), l2)
+    _check(out, lse, q, k, v, idx, w.scale)
+
+
 @pytest.mark.parametrize("hd,out_dtype", [(64, "f32"), (128, "bf16"), (256, "f32"), (20, "f32")])
 def test_lse_merge_entry_point(F, hd, out_dtype):
     g = np.random.default_rng(hd)
