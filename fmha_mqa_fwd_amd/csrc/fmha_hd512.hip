@@ -43,6 +43,9 @@ constexpr int G5_MAX_KEYS = 1024;  // a split's row offsets held in LDS
 // and split within that source; its partial (partial modes) goes to plane
 // `plane`.  gather: the source is a pool read through kv_idx (a constant in
 // the one-source kernels, per workgroup in the several-source one).
+// NT: the K/V DMA is non-temporal (a dense split's keys are read once; in
+// the several-source kernel, where the source decides at run time, plain).
+template <bool NT>
 __device__ __forceinline__ void fwd512_body(const FwdParams& p, const bool gather,
                                             const WgCoords wc, const int plane) {
   constexpr int HD = G5_HD, HDW = HD / 2, QW = 32, KT = 32, WAVES = 4, NKS = KT / 16;
@@ -136,10 +139,10 @@ __device__ __forceinline__ void fwd512_body(const FwdParams& p, const bool gathe
       __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < RPW; ++j)
-      if (gather)  // pool rows are shared between tokens; a split's keys are read once
-        dma16(rsrc, (uint32_t)(uintptr_t)(buf + (wave * RPW + j) * stride), o.o[j]);
-      else
+      if constexpr (NT)
         dma16_nt(rsrc, (uint32_t)(uintptr_t)(buf + (wave * RPW + j) * stride), o.o[j]);
+      else
+        dma16(rsrc, (uint32_t)(uintptr_t)(buf + (wave * RPW + j) * stride), o.o[j]);
   };
   auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd512_kernel(FwdParams p) {
   const WgCoords wc =
       wg_coords(blockIdx.x, p.tiles_per_group, p.n_groups, p.n_groups * p.num_splits);
-  fwd512_body(p, GATHER, wc, wc.split);
+  fwd512_body<!GATHER>(p, GATHER, wc, wc.split);  // gathered pool rows are shared between tokens
 }
 
 // Several key sources in one launch: workgroup blockIdx.x belongs to the last
@@ -253,7 +256,7 @@ void fwd512_sources_kernel(SourcesParams sp) {
   p.tiles_per_group = src.tiles_per_group;
   const WgCoords wc = wg_coords(bid - src.wg_begin, src.tiles_per_group, src.n_groups,
                                 src.n_groups * src.num_splits);
-  fwd512_body(p, src.kv_idx != nullptr, wc, src.plane_begin + wc.split);
+  fwd512_body<false>(p, src.kv_idx != nullptr, wc, src.plane_begin + wc.split);
 }
 
 }  // namespace
