@@ -397,28 +397,33 @@ void fwd_gather_staged_kernel(FwdParams p) {
   struct Offs {
     uint32_t k[KJ], v[VJ];
   };
-  // this lane's DMA offsets for tile t (OOB + column stays out of range)
+  // the list entries of this lane's rows of tile t, read unconditionally (the
+  // tile clamped to the last, a pad slot to row 0: such values are discarded
+  // in issue) so that the reads carry no branch and no wait of their own; the
+  // compiler waits for them where issue uses them, a tile later
   auto offsets = [&](int t) __attribute__((always_inline)) {
     Offs o;
-    const bool live = t < n_tiles;
+    const int base = min(t, n_tiles - 1) * KT;
 #pragma unroll
-    for (int j = 0; j < KJ; ++j)
-      o.k[j] = (live && kr[j] >= 0) ? sOff[t * KT + kr[j]] + (uint32_t)kc[j] : OOB;
+    for (int j = 0; j < KJ; ++j) o.k[j] = sOff[base + max(kr[j], 0)];
 #pragma unroll
-    for (int j = 0; j < VJ; ++j)
-      o.v[j] = (live && vr[j] >= 0) ? sOff[t * KT + vr[j]] + (uint32_t)vc[j] : OOB;
+    for (int j = 0; j < VJ; ++j) o.v[j] = sOff[base + max(vr[j], 0)];
     return o;
   };
-  auto issue = [&](const Offs& o, char* kbuf, char* vbuf) __attribute__((always_inline)) {
+  // tile t's DMA from its list entries (OOB + column stays out of range)
+  auto issue = [&](const Offs& o, int t, char* kbuf, char* vbuf) __attribute__((always_inline)) {
+    const bool live = t < n_tiles;
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
       const int inst = wave + WAVES * j;
-      dma16(rk, (uint32_t)(uintptr_t)(inst < NKI ? kbuf + inst * 1024 : sSpare), o.k[j]);
+      const uint32_t off = (live && kr[j] >= 0) ? o.k[j] + (uint32_t)kc[j] : OOB;
+      dma16(rk, (uint32_t)(uintptr_t)(inst < NKI ? kbuf + inst * 1024 : sSpare), off);
     }
 #pragma unroll
     for (int j = 0; j < VJ; ++j) {
       const int inst = wave + WAVES * j;
-      dma16(rv, (uint32_t)(uintptr_t)(inst < NVI ? vbuf + inst * 1024 : sSpare), o.v[j]);
+      const uint32_t off = (live && vr[j] >= 0) ? o.v[j] + (uint32_t)vc[j] : OOB;
+      dma16(rv, (uint32_t)(uintptr_t)(inst < NVI ? vbuf + inst * 1024 : sSpare), off);
     }
   };
   auto barrier = [&]() __attribute__((always_inline)) {
@@ -439,7 +444,7 @@ void fwd_gather_staged_kernel(FwdParams p) {
 
   auto step = [&](int t, const char* kcur, const char* vcur, char* knext, char* vnext)
       __attribute__((always_inline)) {
-    issue(ahead, knext, vnext);  // tile t+1
+    issue(ahead, t + 1, knext, vnext);  // tile t+1
     ahead = offsets(t + 2);
     f32x16 s[NKB][1];
     w.template qk<NKB>(s, [&](int, int ds) {
@@ -487,7 +492,7 @@ void fwd_gather_staged_kernel(FwdParams p) {
     tile_masked |= (((uint32_t)(b >> 32) != 0) ? 1ull : 0ull) << (r + 1);
   }
   if (n_tiles > 0) {
-    issue(offsets(0), sK0, sV0);
+    issue(offsets(0), 0, sK0, sV0);
     ahead = offsets(1);
     wait_vmcnt<0>();  // tile 0 has landed
     barrier();
