@@ -353,6 +353,7 @@ void fwd_gather_staged_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char sV0[NVI * 1024], sV1[NVI * 1024];
   __shared__ __attribute__((aligned(1024))) char sSpare[1024];
   __shared__ uint32_t sOff[GSW_MAX_KEYS];
+  __shared__ uint32_t sMaskBits[4];  // per wave: its tiles' "has a masked key" bits
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -475,22 +476,28 @@ void fwd_gather_staged_kernel(FwdParams p) {
     idxv[e] = i < nk ? ibase[i] : -1;
   }
   w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf);
+  // entry i = tid + 256e sits in tile i / 32: the 64 entries of wave w in
+  // chunk e are tiles 8e + 2w and 8e + 2w + 1, so each wave finds its tiles'
+  // "has a masked key" bits from its own registers (reading the staged list
+  // back from LDS cost a round trip per tile pair, several µs at a
+  // workgroup's start while the CU's other workgroups stream)
+  static_assert(KT == 32 && IPT * 256 <= 32 * KT && WAVES == 4, "mask bit layout");
+  uint32_t my_bits = 0;
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
     const int i = tid + 256 * e;
-    if (i < n_tiles * KT)
-      sOff[i] = (idxv[e] >= 0 && idxv[e] < p.pool_rows) ? (uint32_t)idxv[e] * ROW : OOB;
+    const bool ok = idxv[e] >= 0 && idxv[e] < p.pool_rows;
+    if (i < n_tiles * KT) sOff[i] = ok ? (uint32_t)idxv[e] * ROW : OOB;
+    const uint64_t b = __ballot(i < n_tiles * KT && !ok);
+    my_bits |= (((uint32_t)b != 0) ? 1u : 0u) << (8 * e + 2 * wave);
+    my_bits |= (((uint32_t)(b >> 32) != 0) ? 1u : 0u) << (8 * e + 2 * wave + 1);
   }
+  if (lane == 0) sMaskBits[wave] = my_bits;
   // Q and the list are in before any DMA is issued, so the compiler's own
   // waits for them stay out of the loop
   wait_vmcnt<0>();
   __syncthreads();
-  for (int r = 0; r < n_tiles; r += 2) {  // each wave reads the list two tiles at a time
-    const int i = r * KT + lane;
-    const uint64_t b = __ballot(i < n_tiles * KT && sOff[min(i, GSW_MAX_KEYS - 1)] == OOB);
-    tile_masked |= (((uint32_t)b != 0) ? 1ull : 0ull) << r;
-    tile_masked |= (((uint32_t)(b >> 32) != 0) ? 1ull : 0ull) << (r + 1);
-  }
+  tile_masked = sMaskBits[0] | sMaskBits[1] | sMaskBits[2] | sMaskBits[3];
   if (n_tiles > 0) {
     issue(offsets(0), 0, sK0, sV0);
     ahead = offsets(1);
