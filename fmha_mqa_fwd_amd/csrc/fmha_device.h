@@ -38,6 +38,9 @@ constexpr float LN2 = 0.6931471805599453f;
 // exponential is then <= 2^12, far inside fp32/bf16 range, and O/l need
 // rescaling on few tiles.
 constexpr float SUM_LIMIT = 4096.0f;
+// LDS operand reads issued ahead of their MFMAs (Rows::qk, Rows::pv)
+constexpr int QK_DEPTH = 4;
+constexpr int PV_DEPTH = 3;
 // gfx9 raw buffer descriptor word 3 (32-bit data, no swizzle, offset mode)
 constexpr int BUF_FLAGS = 0x00020000;
 // Cache-policy operand of the buffer-load builtins: the non-temporal bit
@@ -171,6 +174,27 @@ struct Rows {
   // key block kb (32 keys) and contraction step ds.
   template <int NKB, class KFrag>
   __device__ __forceinline__ void qk(f32x16 (&s)[NKB][NQB], KFrag kfrag) const {
+    // one 32x32 block: the K fragments are read QK_DEPTH steps ahead of
+    // their MFMA (the compiler's own order kept two in flight, and each MFMA
+    // pair waited on LDS; ~0.5% faster per prefill call), same MFMA order
+    if constexpr (NKB == 1 && NQB == 1 && NDS >= QK_DEPTH) {
+      constexpr int D = QK_DEPTH;
+      bf16x8 a[D];
+#pragma unroll
+      for (int i = 0; i < D; ++i) a[i] = kfrag(0, i);
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds % D], qf[0][ds], acc, 0, 0, 0);
+        if (ds + D < NDS) a[ds % D] = kfrag(0, ds + D);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      s[0][0] = acc;
+      return;
+    }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -310,6 +334,22 @@ struct Rows {
   // d block db (keys in the accumulator order described above).
   template <int NKS, class VFrag>
   __device__ __forceinline__ void pv(const bf16x8 (&pf)[NQB][NKS], VFrag vfrag) {
+    // the same for V: fragments PV_DEPTH MFMAs ahead, the MFMAs in (ks, db) order
+    if constexpr (NQB == 1 && NKS * NDB >= PV_DEPTH) {
+      constexpr int N = NKS * NDB, D = PV_DEPTH;
+      bf16x8 a[D];
+#pragma unroll
+      for (int i = 0; i < D; ++i) a[i] = vfrag(i / NDB, i % NDB);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        o[i % NDB][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % D], pf[0][i / NDB],
+                                                                o[i % NDB][0], 0, 0, 0);
+        if (i + D < N) a[i % D] = vfrag((i + D) / NDB, (i + D) % NDB);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
