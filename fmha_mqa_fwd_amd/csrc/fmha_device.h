@@ -170,6 +170,30 @@ struct Rows {
     }
   }
 
+  // The one-block QK^T with mid(ds) run right after the MFMA of step ds: work
+  // whose issue then overlaps the matrix unit (the next tile's DMA).  Same
+  // MFMA order and result as qk.
+  template <class KFrag, class Mid>
+  __device__ __forceinline__ void qk_mid(f32x16 (&s)[1][NQB], KFrag kfrag, Mid mid) const {
+    static_assert(NQB == 1 && NDS >= QK_DEPTH, "one block");
+    constexpr int D = QK_DEPTH;
+    bf16x8 a[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) a[i] = kfrag(0, i);
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      __builtin_amdgcn_sched_barrier(0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds % D], qf[0][ds], acc, 0, 0, 0);
+      if (ds + D < NDS) a[ds % D] = kfrag(0, ds + D);
+      mid(ds);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s[0][0] = acc;
+  }
+
   // S^T[kb][qb] = K_tile . Q^T with kfrag(kb, ds) the 16-byte A fragment of
   // key block kb (32 keys) and contraction step ds.
   template <int NKB, class KFrag>

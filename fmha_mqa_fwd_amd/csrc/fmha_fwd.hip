@@ -148,33 +148,48 @@ void fwd_kernel(FwdParams p) {
     return (idx >= 0 && idx < p.pool_rows) ? idx : -1;
   };
 
+  // Dense keys: the DMA is issued from inline assembly (the compiler tracks
+  // none of it, so it can sit between the MFMAs of QK^T without costing
+  // registers), and every wait for it is explicit.  The descriptors of tile t
+  // cover keys t0 .. key_hi-1: later rows read as zeros.
+  auto dense_rsrc = [&](int t, u32x4& rk4, u32x4& rv4) __attribute__((always_inline)) {
+    const int t0 = key_lo + t * KT;
+    const uint32_t nbytes = (uint32_t)((key_hi - t0) * ROW);
+    rk4 = buffer_rsrc(kbase + (int64_t)t0 * HD, nbytes);
+    rv4 = buffer_rsrc(vbase + (int64_t)t0 * HD, nbytes);
+  };
+  // slot q of this wave's dense DMA of a tile: K instruction j = q (q < KJ), else V j = q - KJ
+  auto dense_slot = [&](int q, const u32x4& rk4, const u32x4& rv4, char* kbuf, char* vbuf)
+      __attribute__((always_inline)) {
+    const bool isk = q < KJ;
+    const int j = isk ? q : q - KJ;
+    const int inst = wave + WAVES * j;
+    if (inst < (isk ? NKI : NVI)) {
+      const int r = isk ? kr[j] : vr[j];
+      const uint32_t off = r >= 0 ? (uint32_t)r * ROW + (uint32_t)(isk ? kc[j] : vc[j]) : OOB;
+      dma16(isk ? rk4 : rv4, (uint32_t)(uintptr_t)((isk ? kbuf : vbuf) + inst * 1024), off);
+    }
+  };
   // DMA of tile t into (kbuf, vbuf); gather rows come from sIdx[ib].
   auto issue = [&](int t, char* kbuf, char* vbuf, int ib) __attribute__((always_inline)) {
-    const int t0 = key_lo + t * KT;
-    __amdgpu_buffer_rsrc_t rk, rv;
-    if constexpr (GATHER) {
-      rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, p.pool_rows * ROW, BUF_FLAGS);
-      rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, p.pool_rows * ROW, BUF_FLAGS);
-    } else {
-      // the descriptor covers keys t0 .. key_hi-1: later rows read as zeros
-      const int nbytes = (key_hi - t0) * ROW;
-      rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)t0 * HD), (short)0, nbytes,
-                                             BUF_FLAGS);
-      rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)t0 * HD), (short)0, nbytes,
-                                             BUF_FLAGS);
+    if constexpr (!GATHER) {
+      u32x4 rk4, rv4;
+      dense_rsrc(t, rk4, rv4);
+#pragma unroll
+      for (int q = 0; q < KJ + VJ; ++q) dense_slot(q, rk4, rv4, kbuf, vbuf);
+      return;
     }
+    __amdgpu_buffer_rsrc_t rk, rv;
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, p.pool_rows * ROW, BUF_FLAGS);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, p.pool_rows * ROW, BUF_FLAGS);
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
       const int inst = wave + WAVES * j;
       if (inst < NKI) {
         uint32_t off = OOB;
         if (kr[j] >= 0) {
-          if constexpr (GATHER) {
-            const int idx = sIdx[ib][kr[j]];
-            off = idx >= 0 ? (uint32_t)idx * ROW + kc[j] : OOB;
-          } else {
-            off = (uint32_t)kr[j] * ROW + kc[j];
-          }
+          const int idx = sIdx[ib][kr[j]];
+          off = idx >= 0 ? (uint32_t)idx * ROW + kc[j] : OOB;
         }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rk, (__attribute__((address_space(3))) void*)(kbuf + inst * 1024), 16, off, 0, 0, 0);
@@ -186,12 +201,8 @@ void fwd_kernel(FwdParams p) {
       if (inst < NVI) {
         uint32_t off = OOB;
         if (vr[j] >= 0) {
-          if constexpr (GATHER) {
-            const int idx = sIdx[ib][vr[j]];
-            off = idx >= 0 ? (uint32_t)idx * ROW + vc[j] : OOB;
-          } else {
-            off = (uint32_t)vr[j] * ROW + vc[j];
-          }
+          const int idx = sIdx[ib][vr[j]];
+          off = idx >= 0 ? (uint32_t)idx * ROW + vc[j] : OOB;
         }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rv, (__attribute__((address_space(3))) void*)(vbuf + inst * 1024), 16, off, 0, 0, 0);
@@ -222,21 +233,39 @@ void fwd_kernel(FwdParams p) {
     const int t0 = key_lo + t * KT;
     const bool have_next = t + 1 < n_tiles;
     int idx_ahead = -1;
+    // dense one-block tiles: the DMA of tile t+1 goes out one instruction
+    // after each QK^T MFMA (its issue then overlaps the matrix unit; ~1%
+    // faster per prefill call than issuing it all before QK^T)
+    constexpr bool MID = !GATHER && NKB == 1 && NQB == 1 && DSPLIT == 1;
     if (have_next) {
       if constexpr (GATHER) {
         // validity of tile t+1 for its K buffer, then its DMA
         if (tid < KT) sValid[vb ^ 1][tid] = sIdx[(t + 1) % 3][tid] >= 0;
         issue(t + 1, knext, vnext, (t + 1) % 3);
         idx_ahead = fetch_idx(t + 2);  // written to LDS after the compute
-      } else {
+      } else if constexpr (!MID) {
         issue(t + 1, knext, vnext, 0);
       }
     }
 
     f32x16 s[NKB][NQB];
-    w.template qk<NKB>(s, [&](int kb, int ds) {
+    auto kfrag = [&](int kb, int ds) __attribute__((always_inline)) {
       return *reinterpret_cast<const bf16x8*>(kcur + k_lane + kb * 32 * KS + ds * 32);
-    });
+    };
+    if constexpr (MID) {
+      constexpr int NDS_ = HDW / 16;
+      u32x4 rk4, rv4;
+      dense_rsrc(t + 1, rk4, rv4);
+      w.qk_mid(s, kfrag, [&](int ds) __attribute__((always_inline)) {
+        if (ds < KJ + VJ && have_next) dense_slot(ds, rk4, rv4, knext, vnext);
+      });
+      if (have_next) {
+#pragma unroll
+        for (int q = NDS_; q < KJ + VJ; ++q) dense_slot(q, rk4, rv4, knext, vnext);
+      }
+    } else {
+      w.template qk<NKB>(s, kfrag);
+    }
     if constexpr (DSPLIT == 2) {
       // S^T = this wave's partial + its partner's (same lanes, same layout)
       f32x4* mine = reinterpret_cast<f32x4*>(sX + (wave * 64 + lane) * 16);
@@ -272,8 +301,10 @@ void fwd_kernel(FwdParams p) {
     if constexpr (GATHER) {
       if (have_next && tid < KT) sIdx[(t + 2) % 3][tid] = idx_ahead;
     }
-    // tile t+1 has landed (this barrier's release fence waits for every DMA)
-    // and no wave reads (kcur, vcur) any more
+    // tile t+1 has landed (dense: the explicit wait; gather: this barrier's
+    // release fence waits for every compiler-tracked DMA) and no wave reads
+    // (kcur, vcur) any more
+    if constexpr (!GATHER) wait_vmcnt<0>();
     __syncthreads();
   };
 
@@ -289,6 +320,7 @@ void fwd_kernel(FwdParams p) {
       __syncthreads();
     }
     issue(0, sK0, sV0, 0);
+    if constexpr (!GATHER) wait_vmcnt<0>();  // tile 0 has landed
     if constexpr (GATHER) {
       const int i2 = fetch_idx(2);
       if (tid < KT) sIdx[2][tid] = i2;
