@@ -443,21 +443,25 @@ void fwd_gather_staged_kernel(FwdParams p) {
     for (int j = 0; j < VJ; ++j) o.v[j] = sOff[base + max(vr[j], 0)];
     return o;
   };
-  // tile t's DMA from its list entries (OOB + column stays out of range)
-  auto issue = [&](const Offs& o, int t, char* kbuf, char* vbuf) __attribute__((always_inline)) {
+  // slot q of tile t's DMA from its list entries: K instruction q (q < KJ),
+  // else V instruction q - KJ (OOB + column stays out of range)
+  auto issue_slot = [&](const Offs& o, int t, int q, char* kbuf, char* vbuf)
+      __attribute__((always_inline)) {
     const bool live = t < n_tiles;
-#pragma unroll
-    for (int j = 0; j < KJ; ++j) {
-      const int inst = wave + WAVES * j;
-      const uint32_t off = (live && kr[j] >= 0) ? o.k[j] + (uint32_t)kc[j] : OOB;
+    if (q < KJ) {
+      const int inst = wave + WAVES * q;
+      const uint32_t off = (live && kr[q] >= 0) ? o.k[q] + (uint32_t)kc[q] : OOB;
       dma16(rk, (uint32_t)(uintptr_t)(inst < NKI ? kbuf + inst * 1024 : sSpare), off);
-    }
-#pragma unroll
-    for (int j = 0; j < VJ; ++j) {
+    } else {
+      const int j = q - KJ;
       const int inst = wave + WAVES * j;
       const uint32_t off = (live && vr[j] >= 0) ? o.v[j] + (uint32_t)vc[j] : OOB;
       dma16(rv, (uint32_t)(uintptr_t)(inst < NVI ? vbuf + inst * 1024 : sSpare), off);
     }
+  };
+  auto issue = [&](const Offs& o, int t, char* kbuf, char* vbuf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < KJ + VJ; ++q) issue_slot(o, t, q, kbuf, vbuf);
   };
   auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
@@ -475,14 +479,20 @@ void fwd_gather_staged_kernel(FwdParams p) {
   Offs ahead;                // offsets of tile t+1, read during tile t-1
   uint64_t tile_masked = 0;  // bit t: tile t has a masked key
 
+  constexpr int NDS = HD / 16;
   auto step = [&](int t, const char* kcur, const char* vcur, char* knext, char* vnext)
       __attribute__((always_inline)) {
-    issue(ahead, t + 1, knext, vnext);  // tile t+1
-    ahead = offsets(t + 2);
+    // tile t+1's DMA, one instruction after each QK^T MFMA (its issue then
+    // overlaps the matrix unit), from the entries read a tile ago
     f32x16 s[NKB][1];
-    w.template qk<NKB>(s, [&](int, int ds) {
+    w.qk_mid(s, [&](int, int ds) __attribute__((always_inline)) {
       return *reinterpret_cast<const bf16x8*>(kcur + k_lane + ds * 32);
+    }, [&](int ds) __attribute__((always_inline)) {
+      if (ds < KJ + VJ) issue_slot(ahead, t + 1, ds, knext, vnext);
     });
+#pragma unroll
+    for (int q = NDS; q < KJ + VJ; ++q) issue_slot(ahead, t + 1, q, knext, vnext);
+    ahead = offsets(t + 2);  // read under this tile's softmax and PV
     if ((tile_masked >> t) & 1) {
       const int kbase = t * KT;
       w.template mask<NKB>(s, hlf, [&](int kk) { return sOff[kbase + kk] != OOB; });
