@@ -135,14 +135,17 @@ __device__ __forceinline__ void fwd512_body(const FwdParams& p, const bool gathe
     }
     return r;
   };
+  auto issue_row = [&](const u32x4& rsrc, const Offs& o, char* buf, int stride, int j)
+      __attribute__((always_inline)) {
+    if constexpr (NT)
+      dma16_nt(rsrc, (uint32_t)(uintptr_t)(buf + (wave * RPW + j) * stride), o.o[j]);
+    else
+      dma16(rsrc, (uint32_t)(uintptr_t)(buf + (wave * RPW + j) * stride), o.o[j]);
+  };
   auto issue = [&](const u32x4& rsrc, const Offs& o, char* buf, int stride)
       __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < RPW; ++j)
-      if constexpr (NT)
-        dma16_nt(rsrc, (uint32_t)(uintptr_t)(buf + (wave * RPW + j) * stride), o.o[j]);
-      else
-        dma16(rsrc, (uint32_t)(uintptr_t)(buf + (wave * RPW + j) * stride), o.o[j]);
+    for (int j = 0; j < RPW; ++j) issue_row(rsrc, o, buf, stride, j);
   };
   auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
@@ -163,10 +166,13 @@ __device__ __forceinline__ void fwd512_body(const FwdParams& p, const bool gathe
   Offs next;  // offsets of tile t+1 (its K is in flight, its V is issued at the start of t)
   auto step = [&](int t, char* kcur, const char* vcur, char* vnext)
       __attribute__((always_inline)) {
-    issue(rv, next, vnext, VS);  // V(t+1)
+    // V(t+1), one row after each of the first RPW QK^T MFMAs (the DMA issue
+    // then overlaps the matrix unit)
     f32x16 s[1][1];
-    w.template qk<1>(s, [&](int, int ds) {
+    w.qk_mid(s, [&](int, int ds) __attribute__((always_inline)) {
       return *reinterpret_cast<const bf16x8*>(kcur + k_lane + ds * 32);
+    }, [&](int ds) __attribute__((always_inline)) {
+      if (ds < RPW) issue_row(rv, next, vnext, VS, ds);
     });
     // S^T = this wave's partial + its partner's (same lanes, same layout)
 #pragma unroll
