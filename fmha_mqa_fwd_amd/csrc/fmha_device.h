@@ -386,6 +386,25 @@ struct Rows {
     }
   }
 
+  // pv with mid(i) run right after its i-th MFMA (the pipelined order above).
+  template <int NKS, class VFrag, class Mid>
+  __device__ __forceinline__ void pv_mid(const bf16x8 (&pf)[NQB][NKS], VFrag vfrag, Mid mid) {
+    static_assert(NQB == 1 && NKS * NDB >= PV_DEPTH, "one block");
+    constexpr int N = NKS * NDB, D = PV_DEPTH;
+    bf16x8 a[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) a[i] = vfrag(i / NDB, i % NDB);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      o[i % NDB][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % D], pf[0][i / NDB],
+                                                              o[i % NDB][0], 0, 0, 0);
+      if (i + D < N) a[i % D] = vfrag((i + D) / NDB, (i + D) % NDB);
+      mid(i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   // O / l and lse = (m + log2 l) ln 2; an empty row (no key seen) gets O = 0,
   // lse = -inf.  Partial modes write plane `split` of [splits, rows, HD].
   // Direct form: each lane stores its own 4-element pieces (a row's 32-wide d

@@ -45,7 +45,10 @@ constexpr int G5_MAX_KEYS = 1024;  // a split's row offsets held in LDS
 // the one-source kernels, per workgroup in the several-source one).
 // NT: the K/V DMA is non-temporal (a dense split's keys are read once; in
 // the several-source kernel, where the source decides at run time, plain).
-template <bool NT>
+// KPV: K(t+2) goes out between the PV MFMAs (measured faster for the gathered
+// Flash top-k, slower for decode's short splits, which keep it right after
+// the S exchange).
+template <bool NT, bool KPV>
 __device__ __forceinline__ void fwd512_body(const FwdParams& p, const bool gather,
                                             const WgCoords wc, const int plane) {
   constexpr int HD = G5_HD, HDW = HD / 2, QW = 32, KT = 32, WAVES = 4, NKS = KT / 16;
@@ -180,7 +183,7 @@ __device__ __forceinline__ void fwd512_body(const FwdParams& p, const bool gathe
       x_mine[i] = f32x4{s[0][0][4 * i], s[0][0][4 * i + 1], s[0][0][4 * i + 2], s[0][0][4 * i + 3]};
     barrier();  // every wave is past QK^T(t): K(t)'s stage is free
     const Offs ahead = offsets(t + 2);
-    issue(rk, ahead, kcur, KS);  // K(t+2)
+    if constexpr (!KPV) issue(rk, ahead, kcur, KS);  // K(t+2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 o = x_theirs[i];
@@ -193,9 +196,13 @@ __device__ __forceinline__ void fwd512_body(const FwdParams& p, const bool gathe
     }
     bf16x8 pf[1][NKS];
     if (w.template softmax<1>(s, pf, c)) w.rescale_o();
-    w.template pv<NKS>(pf, [&](int ks, int db) {
+    w.template pv_mid<NKS>(pf, [&](int ks, int db) __attribute__((always_inline)) {
       const char* a = vcur + v_lane + 16 * ks * VS + 64 * db;
       return v_frag_tr(a, a + 8 * VS);
+    }, [&](int i) __attribute__((always_inline)) {
+      if constexpr (KPV) {
+        if (i < RPW) issue_row(rk, ahead, kcur, KS, i);  // K(t+2)
+      }
     });
     next = ahead;
     // K(t+1) and V(t+1) have landed; K(t+2) may still be in flight
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd512_kernel(FwdParams p) {
   const WgCoords wc =
       wg_coords(blockIdx.x, p.tiles_per_group, p.n_groups, p.n_groups * p.num_splits);
-  fwd512_body<!GATHER>(p, GATHER, wc, wc.split);  // gathered pool rows are shared between tokens
+  fwd512_body<!GATHER, GATHER>(p, GATHER, wc, wc.split);  // gathered pool rows are shared
 }
 
 // Several key sources in one launch: workgroup blockIdx.x belongs to the last
@@ -262,7 +269,7 @@ void fwd512_sources_kernel(SourcesParams sp) {
   p.tiles_per_group = src.tiles_per_group;
   const WgCoords wc = wg_coords(bid - src.wg_begin, src.tiles_per_group, src.n_groups,
                                 src.n_groups * src.num_splits);
-  fwd512_body<false>(p, src.kv_idx != nullptr, wc, src.plane_begin + wc.split);
+  fwd512_body<false, false>(p, src.kv_idx != nullptr, wc, src.plane_begin + wc.split);
 }
 
 }  // namespace
