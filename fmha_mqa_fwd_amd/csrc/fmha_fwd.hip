@@ -30,8 +30,11 @@
 //     conflicts) and the lanes that land on pad bytes read out-of-range zeros,
 //     so every operand read is a per-lane base plus an immediate offset.
 //   * Double buffering: tile t+1 is DMA'd while tile t is computed; each buffer
-//     is its own LDS object and the loop is unrolled by two, so the compiler's
-//     DMA-completion waits stay per buffer.  One barrier per tile.
+//     is its own LDS object and the loop is unrolled by two.  Dense tiles are
+//     DMA'd from inline assembly, one instruction after each QK^T MFMA, and
+//     waited for explicitly before the tile's barrier; gathered tiles use the
+//     compiler-tracked builtin, whose waits the compiler keeps per buffer.
+//     One barrier per tile.
 //   * Several workgroups share a CU where registers allow, so one wave's
 //     softmax overlaps other waves' MFMAs.
 #include <type_traits>
