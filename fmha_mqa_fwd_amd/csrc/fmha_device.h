@@ -577,6 +577,92 @@ __device__ __forceinline__ int swz_v(int row) {
   else return (0x2460 >> (4 * (row & 3))) & 15;                      // 0, 6, 4, 2
 }
 
+// ---- Order of a gathered key list.  Attention does not depend on the order
+// of its keys, so a split's list may be walked in any order.  Walked by pool
+// region, the workgroups that run at one time on an XCD read rows from the same
+// part of the pool and share that XCD's L2 lines; walked in list order (a
+// uniform draw) they read rows from all of it.
+
+// Region class of a list entry: row >> shift over 32 regions of the pool for
+// a usable row, 32 for an entry that reads nothing (it goes last).
+__device__ __forceinline__ int region_shift(int pool_rows) {
+  const int bits = pool_rows > 1 ? 32 - __clz(pool_rows - 1) : 0;  // ceil(log2(pool_rows))
+  return bits > 5 ? bits - 5 : 0;
+}
+constexpr int REGION_NONE = 32;
+// Lists of fewer tiles are walked as given: a decode split of a few tiles
+// gains nothing from the order and its one-round launch pays the sort's
+// time in full (measured: two-source decode 28.8 against 27.7 us sorted).
+constexpr int ORDER_MIN_TILES = 8;
+
+// Stable counting sort of a list of up to 64 * WAVES * SLOTS entries by region
+// class.  Entry i (i < n) is held by lane i % 64 of wave (i / 64) % WAVES in
+// slot (i / 64) / WAVES as (off, cls); it is stored to dst at its position in
+// the ordered list (equal classes keep their list order, so the order, and the
+// kernel's result, are the same on every run).  cnt is LDS scratch of
+// 64 * WAVES * SLOTS ints.  Two workgroup barriers; the caller's barrier must
+// follow before dst is read.  Returns the number of usable entries: they are
+// dst[0 .. n_usable - 1], the unusable ones after them.
+template <int WAVES, int SLOTS>
+__device__ __forceinline__ int order_by_region(const uint32_t (&off)[SLOTS],
+                                               const int (&cls)[SLOTS], int n, uint32_t* dst,
+                                               int* cnt, int wave, int lane) {
+  constexpr int NCH = WAVES * SLOTS;  // 64-entry chunks
+  int rank[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const int ch = wave + WAVES * s;
+    const bool present = 64 * ch + lane < n;
+    uint64_t own = __ballot(present);  // lanes of this chunk in my class
+    uint64_t of_lane = own;            // lanes of this chunk in class `lane`
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+      // lanes whose class has bit b set; kept against per-lane flips (a
+      // per-lane choice between the mask and its complement keeps both in
+      // scalar registers, and the slots' pairs spilled)
+      const uint64_t bb = __ballot(present && ((cls[s] >> b) & 1));
+      own &= bb ^ (((cls[s] >> b) & 1) ? 0ull : ~0ull);
+      of_lane &= bb ^ (((lane >> b) & 1) ? 0ull : ~0ull);
+    }
+    rank[s] = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(own >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)own, 0u));
+    cnt[64 * ch + lane] = __popcll(of_lane);
+    // one slot's masks at a time (interleaved, the slots' ballots spill SGPRs)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // lane = class: each chunk's first position for the class, in class-major
+    // then chunk order
+    int v[NCH];
+    int tot = 0;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      v[ch] = cnt[64 * ch + lane];
+      tot += v[ch];
+    }
+    int x = tot;  // inclusive scan over the 64 classes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    int run = x - tot;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      cnt[64 * ch + lane] = run;
+      run += v[ch];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const int ch = wave + WAVES * s;
+    if (64 * ch + lane < n) dst[cnt[64 * ch + cls[s]] + rank[s]] = off[s];
+  }
+  return cnt[REGION_NONE];  // chunk 0's first position of the unusable class
+}
+
 // A V fragment from two ds_read_b64_tr_b16 reads at byte addresses a0 (keys
 // e = 0..3) and a1 (keys e = 4..7) within LDS.
 __device__ __forceinline__ bf16x8 v_frag_tr(const char* a0, const char* a1) {

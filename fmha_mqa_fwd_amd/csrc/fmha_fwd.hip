@@ -360,6 +360,9 @@ void fwd_kernel(FwdParams p) {
 //     byte offsets (OOB for an invalid entry or a key past the split), and a
 //     per-tile "has a masked key" bit is kept in scalar registers, so the
 //     loop issues no global loads and tests no index per key;
+//   * the list is staged in pool-region order (order_by_region): the result
+//     does not depend on the order of the keys, and the workgroups running at
+//     one time then read rows from the same part of the pool;
 //   * the per-lane DMA offsets of tile t+1 are read from that list one tile
 //     ahead (during tile t-1), so no DMA waits on an LDS read;
 //   * every wave issues the same number of DMA instructions per tile (slots
@@ -388,7 +391,6 @@ void fwd_gather_staged_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char sV0[NVI * 1024], sV1[NVI * 1024];
   __shared__ __attribute__((aligned(1024))) char sSpare[1024];
   __shared__ uint32_t sOff[GSW_MAX_KEYS];
-  __shared__ uint32_t sMaskBits[4];  // per wave: its tiles' "has a masked key" bits
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -510,9 +512,11 @@ void fwd_gather_staged_kernel(FwdParams p) {
     barrier();
   };
 
-  // the split's index list, validated, as pool byte offsets: every entry of
-  // this thread is loaded before any is stored, so the loads (and Q's after
-  // them) are in flight together
+  // the split's index list, validated, as pool byte offsets in pool-region
+  // order (sV1 is the sort's scratch until tile 1 is DMA'd; the splits that
+  // reach this kernel have more keys than the whole-chunk kernel takes, 5
+  // tiles or more).  Every entry of this thread is loaded before any is used,
+  // and Q after them, so all of those loads are in flight together.
   constexpr int IPT = GSW_MAX_KEYS / 256;  // list entries per thread
   int idxv[IPT];
 #pragma unroll
@@ -521,28 +525,27 @@ void fwd_gather_staged_kernel(FwdParams p) {
     idxv[e] = i < nk ? ibase[i] : -1;
   }
   w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf);
-  // entry i = tid + 256e sits in tile i / 32: the 64 entries of wave w in
-  // chunk e are tiles 8e + 2w and 8e + 2w + 1, so each wave finds its tiles'
-  // "has a masked key" bits from its own registers (reading the staged list
-  // back from LDS cost a round trip per tile pair, several µs at a
-  // workgroup's start while the CU's other workgroups stream)
-  static_assert(KT == 32 && IPT * 256 <= 32 * KT && WAVES == 4, "mask bit layout");
-  uint32_t my_bits = 0;
+  static_assert(NVI * 1024 >= GSW_MAX_KEYS / 64 * 64 * 4, "sort scratch");
+  const int n_list = n_tiles * KT;
+  const int sh = region_shift(p.pool_rows);
+  uint32_t offv[IPT];
+  int cls[IPT];
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
-    const int i = tid + 256 * e;
     const bool ok = idxv[e] >= 0 && idxv[e] < p.pool_rows;
-    if (i < n_tiles * KT) sOff[i] = ok ? (uint32_t)idxv[e] * ROW : OOB;
-    const uint64_t b = __ballot(i < n_tiles * KT && !ok);
-    my_bits |= (((uint32_t)b != 0) ? 1u : 0u) << (8 * e + 2 * wave);
-    my_bits |= (((uint32_t)(b >> 32) != 0) ? 1u : 0u) << (8 * e + 2 * wave + 1);
+    offv[e] = ok ? (uint32_t)idxv[e] * ROW : OOB;
+    cls[e] = ok ? idxv[e] >> sh : REGION_NONE;
   }
-  if (lane == 0) sMaskBits[wave] = my_bits;
+  const int n_usable = order_by_region<WAVES, IPT>(offv, cls, n_list, sOff,
+                                                   reinterpret_cast<int*>(sV1), wave, lane);
+  // the entries that read nothing are last: tiles n_usable / KT .. n_tiles - 1
+  // have a masked key (n_tiles <= 32)
+  if (n_usable < n_list)
+    tile_masked = ((1ull << n_tiles) - 1) & ~((1ull << (n_usable / KT)) - 1);
   // Q and the list are in before any DMA is issued, so the compiler's own
   // waits for them stay out of the loop
   wait_vmcnt<0>();
   __syncthreads();
-  tile_masked = sMaskBits[0] | sMaskBits[1] | sMaskBits[2] | sMaskBits[3];
   if (n_tiles > 0) {
     issue(offsets(0), 0, sK0, sV0);
     ahead = offsets(1);

@@ -21,10 +21,12 @@
 //     row share it.  The padding (K +16 bytes, V +64 bytes per row) keeps the
 //     operand reads free of bank conflicts with immediate offsets.
 //   * The split's row offsets are staged in LDS once: gather, the index list
-//     validated into pool byte offsets; dense, the keys' offsets in the
-//     batch's K/V.  OOB marks an invalid entry or a key past the split (the
-//     row reads as zeros and its logit is masked).  A per-tile "has a masked
-//     key" bit lives in scalar registers.
+//     validated into pool byte offsets (in pool-region order when it has
+//     ORDER_MIN_TILES tiles or more: then the workgroups running at one time
+//     read rows from the same part of the pool and share L2 lines); dense,
+//     the keys' offsets in the batch's K/V.  OOB marks an invalid entry or a
+//     key past the split (the row reads as zeros and its logit is masked).  A
+//     per-tile "has a masked key" bit lives in scalar registers.
 //   * Two K and two V stages.  K(t+2) is issued as soon as every wave is past
 //     QK^T(t) (the barrier of the S exchange), V(t+1) at the start of tile t;
 //     each tile ends with a wait that leaves K(t+2) in flight.  The DMA is
@@ -90,20 +92,45 @@ __device__ __forceinline__ void fwd512_body(const FwdParams& p, const bool gathe
   const uint32_t lane16 = 16u * (uint32_t)lane;
 
   // the split's row offsets: gather, the index list validated into pool byte
-  // offsets; dense, the keys' offsets in this batch's K/V
+  // offsets (ordered by pool region if long enough; sX is the sort's scratch
+  // until the loop); dense, the keys' offsets in this batch's K/V.  The list entries
+  // are loaded first and Q after them, so all of those loads are in flight
+  // while the list is ordered.
+  constexpr int SLOTS = G5_MAX_KEYS / 256;
+  int idxv[SLOTS];
   if (gather) {
     const int32_t* ibase = p.kv_idx + (int64_t)group * p.s_k + key_lo;
-    for (int i = tid; i < n_tiles * KT; i += 256) {
-      int idx = -1;
-      if (i < nk) idx = ibase[i];
-      sOff[i] = (idx >= 0 && idx < p.pool_rows) ? (uint32_t)idx * ROW : OOB;
+#pragma unroll
+    for (int e = 0; e < SLOTS; ++e) {
+      const int i = tid + 256 * e;
+      idxv[e] = i < nk ? ibase[i] : -1;
+    }
+  }
+  Rows<HDW, QW, HD> w;
+  w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf, col0);
+  if (gather && n_tiles >= ORDER_MIN_TILES) {
+    const int sh = region_shift(p.pool_rows);
+    uint32_t offv[SLOTS];
+    int cls[SLOTS];
+#pragma unroll
+    for (int e = 0; e < SLOTS; ++e) {
+      const bool ok = idxv[e] >= 0 && idxv[e] < p.pool_rows;
+      offv[e] = ok ? (uint32_t)idxv[e] * ROW : OOB;
+      cls[e] = ok ? idxv[e] >> sh : REGION_NONE;
+    }
+    order_by_region<WAVES, SLOTS>(offv, cls, n_tiles * KT, sOff, reinterpret_cast<int*>(sX),
+                                  wave, lane);
+  } else if (gather) {
+#pragma unroll
+    for (int e = 0; e < SLOTS; ++e) {
+      const int i = tid + 256 * e;
+      if (i < n_tiles * KT)
+        sOff[i] = (idxv[e] >= 0 && idxv[e] < p.pool_rows) ? (uint32_t)idxv[e] * ROW : OOB;
     }
   } else {
     for (int i = tid; i < n_tiles * KT; i += 256)
       sOff[i] = i < nk ? (uint32_t)(key_lo + i) * ROW : OOB;
   }
-  Rows<HDW, QW, HD> w;
-  w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf, col0);
   // Q and the list are in before any DMA is issued, so the compiler's own
   // waits for them stay out of the loop
   wait_vmcnt<0>();

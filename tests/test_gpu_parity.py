@@ -326,6 +326,47 @@ def test_long_split_gather_masks_invalid_entries(F, hd):
 
 
 @pytest.mark.parametrize("hd", [64, 128, 256, 512])
+def test_region_ordered_gather_masks_invalid_entries(F, hd):
+    """Lists of 8 tiles or more are walked in pool-region order (the result
+    does not depend on the key order): invalid entries spread over every
+    region of the list, a whole invalid tile's worth (keys 320..383), repeated
+    rows, and a token with a single valid entry must still give attention over
+    the valid entries alone, each counted as often as it is listed."""
+    P, s_k = 30000, 1000
+    w = W.make_custom(B=1, T=3, n_h=48, hd=hd, s_k=s_k, pool=P, out_dtype="f32", seed=91 + hd)
+    q, k, v, idx = W.make_inputs(w)
+    bad = idx.clone()
+    bad[0, 0, 3:1000:37] = -1
+    bad[0, 0, 320:384] = P
+    bad[0, 0, 500:520] = bad[0, 0, 600:620]    # repeated rows
+    bad[0, 0, 999] = 2 ** 31 - 1
+    bad[0, 1, ::2] = -2 ** 31                  # half the list, every other key
+    bad[0, 2, :] = P + 5
+    bad[0, 2, 431] = idx[0, 2, 431]            # a single valid key
+    out, lse = _run(F, q, k, v, bad, w.scale, torch.float32, 1)
+    for t in range(3):
+        ok = [int(bad[0, t, j]) for j in range(s_k) if 0 <= int(bad[0, t, j]) < P]
+        sub = torch.tensor([[ok]], dtype=torch.int32)
+        _check(out[:, t:t + 1], lse[:, t:t + 1], q[:, t:t + 1], k, v, sub, w.scale)
+    row = v[int(idx[0, 2, 431])].float()
+    assert torch.allclose(out[0, 2].cpu(), row.expand(48, -1), atol=1e-5)
+
+
+@pytest.mark.parametrize("hd,s_k", [(128, 1024), (256, 160), (512, 512), (512, 1024)])
+def test_region_ordered_gather_runs_are_bitwise_identical(F, hd, s_k):
+    """The region order is a stable counting sort (no atomics): repeated calls
+    give the same bits."""
+    w = W.make_custom(B=2, T=4, n_h=64, hd=hd, s_k=s_k, pool=32768, out_dtype="bf16",
+                      seed=5 + hd)
+    q, k, v, idx = W.make_inputs(w)
+    o1, l1 = _run(F, q, k, v, idx, w.scale, torch.bfloat16, 1)
+    for _ in range(2):
+        o2, l2 = _run(F, q, k, v, idx, w.scale, torch.bfloat16, 1)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    _check(o1, l1, q, k, v, idx, w.scale)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
 @pytest.mark.parametrize("splits", [1, 3])
 def test_gather_repeated_indices_count_each_time(F, splits, hd):
     """A pool row listed several times is several keys (each takes its own
