@@ -2,8 +2,11 @@
 // must move (every gathered K and V row of every token), read with the same
 // row-per-16-lanes 16-byte pattern and no attention arithmetic.  Its time is
 // the memory side's floor for that access pattern; the attention kernel's
-// time beside it says how much the compute adds.  Each token's rows are
-// folded into one XOR word so that no load can be dropped.
+// time beside it says how much the compute adds.  A list of up to
+// FLOOR_STAGED keys is read in the pool-region order the attention kernels
+// walk it in (order_by_region), longer lists in list order.  Each token's
+// rows are folded into one XOR word so that no load can be dropped (the word
+// does not depend on the order).
 #include "fmha_device.h"
 
 namespace fmha {
@@ -13,6 +16,7 @@ using dev::u32x4;
 
 constexpr int FLOOR_THREADS = 256;
 constexpr int FLOOR_UNROLL = 8;  // loads in flight per thread
+constexpr int FLOOR_STAGED = 1024;  // longest list staged in LDS in region order
 
 template <int HD>
 __global__ __launch_bounds__(FLOOR_THREADS) void gather_floor_kernel(
@@ -27,16 +31,41 @@ __global__ __launch_bounds__(FLOOR_THREADS) void gather_floor_kernel(
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void*)v, (short)0, pool_rows * ROW, dev::BUF_FLAGS);
   const int total = s_k * CPR;     // chunks of K (and as many of V)
+  __shared__ uint32_t sRow[FLOOR_STAGED];  // the list as pool byte offsets, region order
+  __shared__ int sCnt[FLOOR_STAGED];       // the sort's scratch
+  const bool staged = s_k <= FLOOR_STAGED;
+  if (staged) {
+    constexpr int SLOTS = FLOOR_STAGED / FLOOR_THREADS;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int sh = dev::region_shift(pool_rows);
+    uint32_t offv[SLOTS];
+    int cls[SLOTS];
+#pragma unroll
+    for (int e = 0; e < SLOTS; ++e) {
+      const int i = tid + FLOOR_THREADS * e;
+      const int r = i < s_k ? idx[i] : -1;
+      const bool ok = r >= 0 && r < pool_rows;
+      offv[e] = ok ? (uint32_t)r * ROW : dev::OOB;
+      cls[e] = ok ? r >> sh : dev::REGION_NONE;
+    }
+    dev::order_by_region<FLOOR_THREADS / 64, SLOTS>(offv, cls, s_k, sRow, sCnt, wave, tid & 63);
+    __syncthreads();
+  }
   uint32_t acc = 0;
   for (int base = threadIdx.x; base < total; base += FLOOR_THREADS * FLOOR_UNROLL) {
     u32x4 x[2 * FLOOR_UNROLL];
 #pragma unroll
     for (int u = 0; u < FLOOR_UNROLL; ++u) {
       const int c = base + u * FLOOR_THREADS;
-      uint32_t off = 0x80000000u;  // beyond the descriptor: reads zeros
+      uint32_t off = dev::OOB;  // beyond the descriptor: reads zeros
       if (c < total) {
-        const int r = idx[c / CPR];
-        if (r >= 0 && r < pool_rows) off = (uint32_t)r * ROW + 16u * (c % CPR);
+        if (staged) {
+          const uint32_t ro = sRow[c / CPR];
+          if (ro != dev::OOB) off = ro + 16u * (c % CPR);
+        } else {
+          const int r = idx[c / CPR];
+          if (r >= 0 && r < pool_rows) off = (uint32_t)r * ROW + 16u * (c % CPR);
+        }
       }
       x[2 * u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
       x[2 * u + 1] =

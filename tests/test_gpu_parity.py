@@ -686,13 +686,15 @@ def test_lse_merge_entry_point(F, hd, out_dtype):
 
 
 # ------------------------------------------------- measurement helper
-def test_gather_floor_reads_every_gathered_row(F):
+@pytest.mark.parametrize("hd,s_k", [(128, 100), (512, 512), (64, 1500)])
+def test_gather_floor_reads_every_gathered_row(F, hd, s_k):
     """fmha_gather_floor (the sparse config's gather-only floor) reads each
-    listed K and V row once: its per-token XOR of the words read equals the
+    listed K and V row once, lists of up to 1024 keys in region order and
+    longer ones in list order: its per-token XOR of the words read equals the
     XOR computed on the CPU; masked entries read nothing."""
     dev = torch.device("cuda:0")
-    g = torch.Generator().manual_seed(61)
-    P, hd, B, T, s_k = 500, 128, 2, 3, 100
+    g = torch.Generator().manual_seed(61 + s_k)
+    P, B, T = 500, 2, 3
     k = torch.randn(P, hd, generator=g).to(torch.bfloat16)
     v = torch.randn(P, hd, generator=g).to(torch.bfloat16)
     idx = torch.randint(0, P, (B, T, s_k), generator=g, dtype=torch.int32)
