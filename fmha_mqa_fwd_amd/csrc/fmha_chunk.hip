@@ -169,12 +169,11 @@ void chunk_kernel(FwdParams p) {
   const int jj = lane & 15;
   const int dsub = (lane >> 4) & 1;
 
-#pragma unroll
-  for (int g = 0; g < NGROUP; ++g) {
-    if (g * TPG >= n_tiles) break;
-    // This wave's DMAs of later groups may still be in flight; once the rest
-    // have landed in LDS, a plain s_barrier publishes every wave's share.  (A
-    // __syncthreads() would add a release fence, i.e. wait for all of them.)
+  // Group g's keys are usable once this wave's DMAs up to group g have
+  // landed (later groups may still be in flight) and a plain s_barrier has
+  // published every wave's share.  (A __syncthreads() would add a release
+  // fence, i.e. wait for all of them.)
+  auto ready = [&](int g) __attribute__((always_inline)) {
     switch (g) {  // g is unrolled away; the wait needs an immediate count
       case 0: wait_vmcnt<2 * IPW * (NGROUP - 1)>(); break;
       case 1: wait_vmcnt<2 * IPW * (NGROUP - 2)>(); break;
@@ -183,43 +182,71 @@ void chunk_kernel(FwdParams p) {
     }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const char* sk = kgrp(g);
-    const char* sv = vgrp(g);
-#pragma unroll
-    for (int tt = 0; tt < TPG; ++tt) {
-      const int t = g * TPG + tt;
-      if (t >= n_tiles) break;
-      const int kt0 = t * KT;   // first key of the tile within the chunk
-      const int lt0 = tt * KT;  // its first row within the group's LDS object
-      bool any_masked = false;
-      if constexpr (GATHER) any_masked = __any(lane < KT && !sValid[kt0 + (lane & (KT - 1))]);
-
-      f32x16 s[1][NQB];
-      const int krow = lt0 + l32;
-      const char* kr = sk + krow * ROW;
-      const int kx = swz_k<CPR>(g * GK + krow);
-      w.template qk<1>(s, [&](int, int ds) {
-        return *reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * ds + hlf) ^ kx));
-      });
-      const bool tail = (kt0 + KT > nk);
-      if (tail || (GATHER && any_masked)) {
-        w.template mask<1>(s, hlf, [&](int kk) {
-          const int key = kt0 + kk;
-          if constexpr (GATHER) return key < nk && sValid[key] != 0;
-          return key < nk;
-        });
-      }
-      bf16x8 pf[NQB][NKS];
-      if (w.template softmax<1>(s, pf, c)) w.rescale_o();
-      w.template pv<NKS>(pf, [&](int ks, int db) {
-        const int r0 = lt0 + 16 * ks + 4 * hlf + (jj >> 2);
-        const int r1 = r0 + 8;
-        const int ch = 4 * db + 2 * dsub + ((jj & 3) >> 1);
-        const int sub = 8 * (jj & 1);
-        return v_frag_tr(sv + r0 * ROW + 16 * (ch ^ swz_v<CPR>(g * GK + r0)) + sub,
-                         sv + r1 * ROW + 16 * (ch ^ swz_v<CPR>(g * GK + r1)) + sub);
+  };
+  // the K fragments of tile t (its group's LDS object, row-swizzled chunks)
+  auto kfrag_of = [&](int t) __attribute__((always_inline)) {
+    const int g = t / TPG;
+    const int krow = (t % TPG) * KT + l32;
+    const char* kr = kgrp(g) + krow * ROW;
+    const int kx = swz_k<CPR>(g * GK + krow);
+    return [=](int, int ds) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * ds + hlf) ^ kx));
+    };
+  };
+  // -inf for tile t's keys past the split or (gather) unusable
+  auto mask_tile = [&](int t, f32x16 (&s)[1][NQB]) __attribute__((always_inline)) {
+    const int kt0 = t * KT;
+    bool any_masked = false;
+    if constexpr (GATHER) any_masked = __any(lane < KT && !sValid[kt0 + (lane & (KT - 1))]);
+    if (kt0 + KT > nk || (GATHER && any_masked)) {
+      w.template mask<1>(s, hlf, [&](int kk) {
+        const int key = kt0 + kk;
+        if constexpr (GATHER) return key < nk && sValid[key] != 0;
+        return key < nk;
       });
     }
+  };
+
+  // Software pipeline over the chunk's tiles: the QK^T MFMAs of tile t+1
+  // carry tile t's exponentials (qk_next_softmax), then PV of tile t.  With
+  // one wave per SIMD nothing else would overlap a tile's softmax.
+  constexpr int MAXT = MAXK / KT;
+  f32x16 s[1][NQB];
+  if (n_tiles > 0) {
+    ready(0);
+    w.template qk<1>(s, kfrag_of(0));
+    mask_tile(0, s);
+  }
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    if (t >= n_tiles) break;
+    const bool has_next = t + 1 < n_tiles;
+    if (has_next && (t + 1) % TPG == 0) ready((t + 1) / TPG);
+    bf16x8 pf[NQB][NKS];
+    float ls[NQB];
+    f32x16 s_next[1][NQB];
+    bool redo;
+    if (has_next) {
+      redo = w.qk_next_softmax(s_next, kfrag_of(t + 1), s, pf, c, ls);
+    } else {
+      redo = w.template softmax_fast<1>(s, pf, c, ls);
+    }
+    if (redo) w.template softmax_slow<1>(s, pf, c, ls);
+    w.commit_l(ls);
+    if (redo) w.rescale_o();
+    if (has_next) mask_tile(t + 1, s_next);
+    const int g = t / TPG;
+    const int lt0 = (t % TPG) * KT;  // the tile's first row within its group's LDS object
+    const char* sv = vgrp(g);
+    w.template pv<NKS>(pf, [&](int ks, int db) {
+      const int r0 = lt0 + 16 * ks + 4 * hlf + (jj >> 2);
+      const int r1 = r0 + 8;
+      const int ch = 4 * db + 2 * dsub + ((jj & 3) >> 1);
+      const int sub = 8 * (jj & 1);
+      return v_frag_tr(sv + r0 * ROW + 16 * (ch ^ swz_v<CPR>(g * GK + r0)) + sub,
+                       sv + r1 * ROW + 16 * (ch ^ swz_v<CPR>(g * GK + r1)) + sub);
+    });
+    if (has_next) s[0][0] = s_next[0][0];
   }
   // Epilogue through LDS (the K/V groups are free once every wave is past
   // its last tile): wave w stages rows 0-15 in K group w, 16-31 in V group w.

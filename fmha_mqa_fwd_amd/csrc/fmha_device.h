@@ -282,6 +282,65 @@ struct Rows {
     return ls0 + ls1;
   }
 
+  // S^T of the next tile (one 32x32 block, as qk) with the fast-path
+  // exponentials of the current tile (as softmax_fast) spread between its
+  // MFMAs: with one wave per SIMD the next tile's matrix work then runs
+  // while this wave's vector unit takes the exponentials.  Same operations in
+  // the same order per value as qk and softmax_fast, so the same bits; returns
+  // softmax_fast's verdict.
+  template <class KFrag>
+  __device__ __forceinline__ bool qk_next_softmax(f32x16 (&s_next)[1][NQB], KFrag kfrag,
+                                                  const f32x16 (&s_cur)[1][NQB],
+                                                  bf16x8 (&pf)[NQB][2], float c,
+                                                  float (&ls)[NQB]) const {
+    static_assert(NQB == 1 && NDS >= QK_DEPTH && 16 % NDS == 0, "one block");
+    constexpr int D = QK_DEPTH, PER = 16 / NDS;  // exponentials per MFMA
+    bf16x8 a[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) a[i] = kfrag(0, i);
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    const float mu = m[0];
+    float e[16];
+    u32x4 w[2];
+    float ls0, ls1;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      __builtin_amdgcn_sched_barrier(0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds % D], qf[0][ds], acc, 0, 0, 0);
+      if (ds + D < NDS) a[ds % D] = kfrag(0, ds + D);
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int j = ds * PER + u;
+        e[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[0][0][j], c, -mu));
+        // empty asm "writing" each value where it is made: it keeps the
+        // compiler from sinking the slice's work below the later MFMAs
+        asm volatile("" : "+v"(e[j]));
+        if (j & 1) {
+          const int k = j >> 1;  // pair k = 4h + i: word i of fragment h
+          uint32_t pk = pack_bf16x2(e[j - 1], e[j]);
+          asm volatile("" : "+v"(pk));
+          w[k >> 2][k & 3] = pk;
+          if (k == 0) {
+            ls0 = e[0];
+            ls1 = e[1];
+          } else {
+            ls0 += e[j - 1];
+            ls1 += e[j];
+          }
+          asm volatile("" : "+v"(ls0), "+v"(ls1));
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s_next[0][0] = acc;
+    pf[0][0] = __builtin_bit_cast(bf16x8, w[0]);
+    pf[0][1] = __builtin_bit_cast(bf16x8, w[1]);
+    ls[0] = ls0 + ls1;
+    return __any(!(ls[0] <= SUM_LIMIT));
+  }
+
   // Online softmax of one tile in base 2 (x*scale*log2e - m in one FMA), in
   // two halves.  softmax_fast takes the exponentials against the running max
   // as it is and returns (wave-uniform) whether they must be redone: some
