@@ -390,7 +390,7 @@ void fwd_gather_staged_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char sK0[NKI * 1024], sK1[NKI * 1024];
   __shared__ __attribute__((aligned(1024))) char sV0[NVI * 1024], sV1[NVI * 1024];
   __shared__ __attribute__((aligned(1024))) char sSpare[1024];
-  __shared__ uint32_t sOff[GSW_MAX_KEYS];
+  __shared__ uint32_t sOff[GSW_MAX_KEYS + KT];  // the list, then a tile of OOB
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -420,7 +420,7 @@ void fwd_gather_staged_kernel(FwdParams p) {
     const int pos = inst * 1024 + lane * 16;
     const int r = pos / KS, cc = pos % KS;
     kr[j] = (inst < NKI && cc < ROW && r < KT) ? r : -1;
-    kc[j] = cc;
+    kc[j] = kr[j] >= 0 ? cc : 0xFFFFFFFF;  // a pad lane's offset saturates past any pool
   }
 #pragma unroll
   for (int j = 0; j < VJ; ++j) {
@@ -428,45 +428,48 @@ void fwd_gather_staged_kernel(FwdParams p) {
     const int pos = inst * 1024 + lane * 16;
     const int r = pos / VS, cc = pos % VS;
     vr[j] = (inst < NVI && cc < ROW && r < KT) ? r : -1;
-    vc[j] = cc;
+    vc[j] = vr[j] >= 0 ? cc : 0xFFFFFFFF;
   }
   const u32x4 rk = buffer_rsrc(p.k, (uint32_t)p.pool_rows * ROW);
   const u32x4 rv = buffer_rsrc(p.v, (uint32_t)p.pool_rows * ROW);
   struct Offs {
     uint32_t k[KJ], v[VJ];
   };
-  // the list entries of this lane's rows of tile t, read unconditionally (the
-  // tile clamped to the last, a pad slot to row 0: such values are discarded
-  // in issue) so that the reads carry no branch and no wait of their own; the
-  // compiler waits for them where issue uses them, a tile later
+  // the list entries of this lane's rows of tile t, read unconditionally (a
+  // tile past the last reads the OOB tile after the list, a pad slot row 0,
+  // whose value its column then pushes out of range) so that the reads carry
+  // no branch and no wait of their own; the compiler waits for them where
+  // issue uses them, a tile later
   auto offsets = [&](int t) __attribute__((always_inline)) {
     Offs o;
-    const int base = min(t, n_tiles - 1) * KT;
+    const int base = min(t, n_tiles) * KT;
 #pragma unroll
     for (int j = 0; j < KJ; ++j) o.k[j] = sOff[base + max(kr[j], 0)];
 #pragma unroll
     for (int j = 0; j < VJ; ++j) o.v[j] = sOff[base + max(vr[j], 0)];
     return o;
   };
-  // slot q of tile t's DMA from its list entries: K instruction q (q < KJ),
-  // else V instruction q - KJ (OOB + column stays out of range)
-  auto issue_slot = [&](const Offs& o, int t, int q, char* kbuf, char* vbuf)
+  // slot q of a tile's DMA from its list entries: K instruction q (q < KJ),
+  // else V instruction q - KJ.  Entry + column in one saturating add: a
+  // usable row's offset plus its column stays inside the pool; OOB (2^31,
+  // beyond any pool's byte count) plus a column, or anything plus a pad
+  // lane's all-ones column, lands past the pool and reads zeros.
+  auto issue_slot = [&](const Offs& o, int q, char* kbuf, char* vbuf)
       __attribute__((always_inline)) {
-    const bool live = t < n_tiles;
     if (q < KJ) {
       const int inst = wave + WAVES * q;
-      const uint32_t off = (live && kr[q] >= 0) ? o.k[q] + (uint32_t)kc[q] : OOB;
+      const uint32_t off = __builtin_elementwise_add_sat(o.k[q], (uint32_t)kc[q]);
       dma16(rk, (uint32_t)(uintptr_t)(inst < NKI ? kbuf + inst * 1024 : sSpare), off);
     } else {
       const int j = q - KJ;
       const int inst = wave + WAVES * j;
-      const uint32_t off = (live && vr[j] >= 0) ? o.v[j] + (uint32_t)vc[j] : OOB;
+      const uint32_t off = __builtin_elementwise_add_sat(o.v[j], (uint32_t)vc[j]);
       dma16(rv, (uint32_t)(uintptr_t)(inst < NVI ? vbuf + inst * 1024 : sSpare), off);
     }
   };
-  auto issue = [&](const Offs& o, int t, char* kbuf, char* vbuf) __attribute__((always_inline)) {
+  auto issue = [&](const Offs& o, char* kbuf, char* vbuf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < KJ + VJ; ++q) issue_slot(o, t, q, kbuf, vbuf);
+    for (int q = 0; q < KJ + VJ; ++q) issue_slot(o, q, kbuf, vbuf);
   };
   auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
@@ -493,10 +496,10 @@ void fwd_gather_staged_kernel(FwdParams p) {
     w.qk_mid(s, [&](int, int ds) __attribute__((always_inline)) {
       return *reinterpret_cast<const bf16x8*>(kcur + k_lane + ds * 32);
     }, [&](int ds) __attribute__((always_inline)) {
-      if (ds < KJ + VJ) issue_slot(ahead, t + 1, ds, knext, vnext);
+      if (ds < KJ + VJ) issue_slot(ahead, ds, knext, vnext);
     });
 #pragma unroll
-    for (int q = NDS; q < KJ + VJ; ++q) issue_slot(ahead, t + 1, q, knext, vnext);
+    for (int q = NDS; q < KJ + VJ; ++q) issue_slot(ahead, q, knext, vnext);
     ahead = offsets(t + 2);  // read under this tile's softmax and PV
     if ((tile_masked >> t) & 1) {
       const int kbase = t * KT;
@@ -542,12 +545,13 @@ void fwd_gather_staged_kernel(FwdParams p) {
   // have a masked key (n_tiles <= 32)
   if (n_usable < n_list)
     tile_masked = ((1ull << n_tiles) - 1) & ~((1ull << (n_usable / KT)) - 1);
+  if (tid < KT) sOff[n_list + tid] = OOB;  // what tiles past the last read
   // Q and the list are in before any DMA is issued, so the compiler's own
   // waits for them stay out of the loop
   wait_vmcnt<0>();
   __syncthreads();
   if (n_tiles > 0) {
-    issue(offsets(0), 0, sK0, sV0);
+    issue(offsets(0), sK0, sV0);
     ahead = offsets(1);
     wait_vmcnt<0>();  // tile 0 has landed
     barrier();
