@@ -117,6 +117,7 @@ def _top_and_window(B, T, n_h, hd, pool, top_k, window, seed, mask=True):
 
 @pytest.mark.parametrize("hd,B,T,n_h,pool,top_k,window,splits", [
     (512, 2, 1, 64, 4096, 512, 128, (4, 2)),   # one launch, the decode shape
+    (512, 2, 2, 32, 4096, 600, 128, (1, 1)),   # one launch; a 19-tile list in region order
     (512, 2, 3, 24, 2048, 300, 70, (3, 2)),    # one launch; token groups beside batch groups
     (512, 1, 2, 8, 512, 0, 40, (1, 1)),        # an empty top-k source
     (512, 3, 1, 16, 1024, 100, 33, (1, 3)),
