@@ -413,14 +413,15 @@ void fwd_gather_staged_kernel(FwdParams p) {
   // DMA geometry (as fwd_kernel): slot j of this wave is instruction
   // wave + 4j, whose lane `lane` fills tile bytes [1024 inst + 16 lane, +16):
   // row r (-1: pad bytes, past the tile, or a spare slot) and column byte c
-  int kr[KJ], kc[KJ], vr[VJ], vc[VJ];
+  int kr[KJ], vr[VJ];
+  uint32_t kc[KJ], vc[VJ];
 #pragma unroll
   for (int j = 0; j < KJ; ++j) {
     const int inst = wave + WAVES * j;
     const int pos = inst * 1024 + lane * 16;
     const int r = pos / KS, cc = pos % KS;
     kr[j] = (inst < NKI && cc < ROW && r < KT) ? r : -1;
-    kc[j] = kr[j] >= 0 ? cc : 0xFFFFFFFF;  // a pad lane's offset saturates past any pool
+    kc[j] = kr[j] >= 0 ? (uint32_t)cc : 0xFFFFFFFFu;  // a pad lane's offset saturates past any pool
   }
 #pragma unroll
   for (int j = 0; j < VJ; ++j) {
@@ -428,7 +429,7 @@ void fwd_gather_staged_kernel(FwdParams p) {
     const int pos = inst * 1024 + lane * 16;
     const int r = pos / VS, cc = pos % VS;
     vr[j] = (inst < NVI && cc < ROW && r < KT) ? r : -1;
-    vc[j] = vr[j] >= 0 ? cc : 0xFFFFFFFF;
+    vc[j] = vr[j] >= 0 ? (uint32_t)cc : 0xFFFFFFFFu;
   }
   const u32x4 rk = buffer_rsrc(p.k, (uint32_t)p.pool_rows * ROW);
   const u32x4 rv = buffer_rsrc(p.v, (uint32_t)p.pool_rows * ROW);
@@ -458,12 +459,12 @@ void fwd_gather_staged_kernel(FwdParams p) {
       __attribute__((always_inline)) {
     if (q < KJ) {
       const int inst = wave + WAVES * q;
-      const uint32_t off = __builtin_elementwise_add_sat(o.k[q], (uint32_t)kc[q]);
+      const uint32_t off = __builtin_elementwise_add_sat(o.k[q], kc[q]);
       dma16(rk, (uint32_t)(uintptr_t)(inst < NKI ? kbuf + inst * 1024 : sSpare), off);
     } else {
       const int j = q - KJ;
       const int inst = wave + WAVES * j;
-      const uint32_t off = __builtin_elementwise_add_sat(o.v[j], (uint32_t)vc[j]);
+      const uint32_t off = __builtin_elementwise_add_sat(o.v[j], vc[j]);
       dma16(rv, (uint32_t)(uintptr_t)(inst < NVI ? vbuf + inst * 1024 : sSpare), off);
     }
   };
