@@ -132,10 +132,17 @@ void score_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       float a[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
+      // ReLU as one integer max of the bit pattern with 0 (a set sign bit is a
+      // negative int: -x and -0 become +0, the rest is kept); fmaxf compiled
+      // to two v_max_f32 per value, the first quieting a signalling NaN that
+      // an MFMA result cannot be
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) a[r & 3] = fmaf(wr[hb][r], fmaxf(s[kb][hb][r], 0.f), a[r & 3]);
+        for (int r = 0; r < 16; ++r) {
+          const float relu = __int_as_float(max(__float_as_int(s[kb][hb][r]), 0));
+          a[r & 3] = fmaf(wr[hb][r], relu, a[r & 3]);
+        }
       const float acc = pair_sum((a[0] + a[1]) + (a[2] + a[3]));
       const int e = e0 + kb * 32 + l32;
       if (live && hlf == 0 && e < P) scores[(int64_t)token * P + e] = acc;
