@@ -352,6 +352,33 @@ def test_region_ordered_gather_masks_invalid_entries(F, hd):
     assert torch.allclose(out[0, 2].cpu(), row.expand(48, -1), atol=1e-5)
 
 
+@pytest.mark.parametrize("hd,P", [(64, 1 << 20), (128, 1), (512, 3)])
+def test_region_ordered_gather_pool_extremes(F, hd, P):
+    """Region classes come from the pool's size (row >> shift, 32 regions):
+    a 2^20-row pool (shift 15) with its first and last rows listed, and pools
+    of 1 and 3 rows (shift 0, every key a repeat), all through lists long
+    enough to be ordered."""
+    s_k = 700
+    w = W.make_custom(B=1, T=2, n_h=16, hd=hd, s_k=s_k, pool=4096, out_dtype="f32",
+                      seed=77 + hd)
+    q, k, v, _ = W.make_inputs(w)
+    g = torch.Generator().manual_seed(78 + hd)
+    if P > 4096:
+        k = torch.randn(P, hd, generator=g).to(torch.bfloat16)
+        v = torch.randn(P, hd, generator=g).to(torch.bfloat16)
+    else:
+        k, v = k[:P].contiguous(), v[:P].contiguous()
+    idx = torch.randint(0, P, (1, 2, s_k), generator=g, dtype=torch.int32)
+    idx[0, 0, 3] = 0
+    idx[0, 0, 500] = P - 1
+    idx[0, 1, 17] = -1
+    out, lse = _run(F, q, k, v, idx, w.scale, torch.float32, 1)
+    for t in range(2):
+        ok = [int(e) for e in idx[0, t].tolist() if 0 <= int(e) < P]
+        sub = torch.tensor([[ok]], dtype=torch.int32)
+        _check(out[:, t:t + 1], lse[:, t:t + 1], q[:, t:t + 1], k, v, sub, w.scale)
+
+
 @pytest.mark.parametrize("hd,s_k", [(128, 1024), (256, 160), (512, 512), (512, 1024)])
 def test_region_ordered_gather_runs_are_bitwise_identical(F, hd, s_k):
     """The region order is a stable counting sort (no atomics): repeated calls
