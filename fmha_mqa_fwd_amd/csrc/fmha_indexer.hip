@@ -13,7 +13,7 @@
 // score_kernel: S = Q_t . K^T with v_mfma_f32_32x32x16_bf16, the A operand
 // being 32 index heads of one token (Q in VGPRs for the whole kernel) and the
 // B operand 32 pool entries (K tiles moved global -> LDS by LDS-DMA, double
-// buffered, shared by the 8 tokens of a workgroup).  In the 32x32 output a
+// buffered, shared by the 4 tokens of a workgroup).  In the 32x32 output a
 // lane holds one entry and 16 of the 32 heads, so the weighted ReLU sum over
 // heads is in-lane plus one v_permlane32_swap.
 //
@@ -31,7 +31,10 @@ namespace {
 
 using namespace dev;
 
-constexpr int IDX_WAVES = 8;  // tokens per score workgroup (one per wave)
+// Tokens per score workgroup (one per wave).  Four, so that the two waves a
+// SIMD runs come from two workgroups, whose per-tile barriers do not keep them
+// in the same phase (eight: 869.7 us per bench call against 857.5; two: 964).
+constexpr int IDX_WAVES = 4;
 constexpr int IDX_KT = 64;    // pool entries per K tile
 constexpr uint32_t IDX_OOB = 0x80000000u;
 
