@@ -265,6 +265,178 @@ __device__ __forceinline__ void fwd512_body(const FwdParams& p, const bool gathe
   w.store(p, grow0, row0, plane, l32, hlf, col0, dh == 0);
 }
 
+// Long gathered splits, two workgroups per CU: one K and one V stage (72 KiB of
+// LDS), the S exchange in the K stage once every wave is past QK^T, K(t+1)
+// issued after the exchange and V(t+1) after PV(t).  A workgroup waits for
+// each tile; the other workgroup on its CU computes meanwhile.
+__device__ __forceinline__ void fwd512_pair_body(const FwdParams& p, const WgCoords wc,
+                                                 const int plane) {
+  constexpr int HD = G5_HD, HDW = HD / 2, QW = 32, KT = 32, WAVES = 4, NKS = KT / 16;
+  constexpr int M_WG = 2 * QW;
+  constexpr int ROW = HD * 2;
+  constexpr int KS = ROW + 16;
+  constexpr int VS = ROW + 64;
+  constexpr int RPW = KT / WAVES;
+  static_assert(ROW == 64 * 16, "one DMA instruction per row");
+  static_assert(WAVES * 64 * 16 * 4 <= KT * KS, "S exchange in the K stage");
+
+  __shared__ __attribute__((aligned(16))) char sK[KT * KS];
+  __shared__ __attribute__((aligned(16))) char sV[KT * VS];
+  __shared__ __attribute__((aligned(16))) uint32_t sOff[G5_MAX_KEYS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hlf = lane >> 5;
+  const int dh = wave & 1;
+  const int col0 = dh * HDW;
+  const int tile = wc.tile, group = wc.group;
+  const int key_lo = wc.split * p.chunk;
+  const int key_hi = min(key_lo + p.chunk, p.s_k);
+  const int nk = max(key_hi - key_lo, 0);
+  const int n_tiles = (nk + KT - 1) / KT;
+  const int row0 = tile * M_WG + (wave >> 1) * QW;
+  const int64_t grow0 = (int64_t)group * p.rows_per_group;
+  const u32x4 rk = buffer_rsrc(p.k, (uint32_t)p.pool_rows * ROW);
+  const u32x4 rv = buffer_rsrc(p.v, (uint32_t)p.pool_rows * ROW);
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+
+  // the list, validated and (ORDER_MIN_TILES tiles or more) in pool-region
+  // order; sV is the sort's scratch before the first V DMA
+  constexpr int SLOTS = G5_MAX_KEYS / 256;
+  int idxv[SLOTS];
+  {
+    const int32_t* ibase = p.kv_idx + (int64_t)group * p.s_k + key_lo;
+#pragma unroll
+    for (int e = 0; e < SLOTS; ++e) {
+      const int i = tid + 256 * e;
+      idxv[e] = i < nk ? ibase[i] : -1;
+    }
+  }
+  Rows<HDW, QW, HD> w;
+  w.load_q(p.q, grow0, row0, p.rows_per_group, l32, hlf, col0);
+  if (n_tiles >= ORDER_MIN_TILES) {
+    const int sh = region_shift(p.pool_rows);
+    uint32_t offv[SLOTS];
+    int cls[SLOTS];
+#pragma unroll
+    for (int e = 0; e < SLOTS; ++e) {
+      const bool ok = idxv[e] >= 0 && idxv[e] < p.pool_rows;
+      offv[e] = ok ? (uint32_t)idxv[e] * ROW : OOB;
+      cls[e] = ok ? idxv[e] >> sh : REGION_NONE;
+    }
+    order_by_region<WAVES, SLOTS>(offv, cls, n_tiles * KT, sOff, reinterpret_cast<int*>(sV),
+                                  wave, lane);
+  } else {
+#pragma unroll
+    for (int e = 0; e < SLOTS; ++e) {
+      const int i = tid + 256 * e;
+      if (i < n_tiles * KT)
+        sOff[i] = (idxv[e] >= 0 && idxv[e] < p.pool_rows) ? (uint32_t)idxv[e] * ROW : OOB;
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  uint64_t tile_masked = 0;
+  for (int r = 0; r < n_tiles; r += 2) {
+    const int i = r * KT + lane;
+    const uint64_t b = __ballot(i < n_tiles * KT && sOff[min(i, G5_MAX_KEYS - 1)] == OOB);
+    tile_masked |= (((uint32_t)b != 0) ? 1ull : 0ull) << r;
+    tile_masked |= (((uint32_t)(b >> 32) != 0) ? 1ull : 0ull) << (r + 1);
+  }
+  // the scratch (sV) and the list are read before any DMA lands in sV
+  __syncthreads();
+
+  auto issue = [&](const u32x4& rsrc, int t, char* buf, int stride) __attribute__((always_inline)) {
+    uint32_t o[RPW];
+    if (t < n_tiles) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(sOff + t * KT + wave * RPW);
+#pragma unroll
+      for (int h = 0; h < RPW / 4; ++h) {
+        const u32x4 x = src[h];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[4 * h + e] = x[e] + lane16;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) o[j] = OOB;
+    }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+      dma16(rsrc, (uint32_t)(uintptr_t)(buf + (wave * RPW + j) * stride), o[j]);
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  };
+  const float c = p.scale_log2;
+  const int jj = lane & 15;
+  const int dsub = (lane >> 4) & 1;
+  const int k_lane = l32 * KS + 16 * hlf + 2 * col0;
+  const int v_lane = (4 * hlf + (jj >> 2)) * VS + 2 * (16 * dsub + 4 * (jj & 3)) + 2 * col0;
+  float* const sX = reinterpret_cast<float*>(sK);
+  f32x4* const x_mine = reinterpret_cast<f32x4*>(sX + (wave * 64 + lane) * 16);
+  const f32x4* const x_theirs = reinterpret_cast<const f32x4*>(sX + ((wave ^ 1) * 64 + lane) * 16);
+
+  if (n_tiles > 0) {
+    issue(rk, 0, sK, KS);
+    issue(rv, 0, sV, VS);
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    wait_vmcnt<0>();
+    barrier();  // K(t) and V(t) have landed
+    f32x16 s[1][1];
+    w.template qk<1>(s, [&](int, int ds) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(sK + k_lane + ds * 32);
+    });
+    barrier();  // every wave is past QK^T(t): the K stage holds the exchange
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x_mine[i] = f32x4{s[0][0][4 * i], s[0][0][4 * i + 1], s[0][0][4 * i + 2], s[0][0][4 * i + 3]};
+    barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 o = x_theirs[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[0][0][4 * i + e] += o[e];
+    }
+    barrier();  // every partial is read: K(t+1) may land
+    issue(rk, t + 1, sK, KS);
+    if ((tile_masked >> t) & 1) {
+      const int kbase = t * KT;
+      w.template mask<1>(s, hlf, [&](int kk) { return sOff[kbase + kk] != OOB; });
+    }
+    bf16x8 pf[1][NKS];
+    if (w.template softmax<1>(s, pf, c)) w.rescale_o();
+    w.template pv<NKS>(pf, [&](int ks, int db) __attribute__((always_inline)) {
+      const char* a = sV + v_lane + 16 * ks * VS + 64 * db;
+      return v_frag_tr(a, a + 8 * VS);
+    });
+    barrier();  // every wave is past PV(t): V(t+1) may land
+    issue(rv, t + 1, sV, VS);
+  }
+  wait_vmcnt<0>();
+  barrier();
+  constexpr int RB_BF16 = HDW * 2;
+  static_assert(2 * QW * RB_BF16 <= KT * KS, "epilogue staging");
+  if (is_bf16(p.out_mode)) {
+    char* const region = ((wave >> 1) == 0 ? sK : sV) + dh * QW * RB_BF16;
+    w.store_lds(p, grow0, row0, plane, lane, [&](int r) { return region + r * RB_BF16; }, col0,
+                dh == 0);
+    return;
+  }
+  w.store(p, grow0, row0, plane, l32, hlf, col0, dh == 0);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd512_pair_kernel(FwdParams p) {
+  const WgCoords wc =
+      wg_coords(blockIdx.x, p.tiles_per_group, p.n_groups, p.n_groups * p.num_splits);
+  fwd512_pair_body(p, wc, wc.split);
+}
+
 template <bool GATHER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd512_kernel(FwdParams p) {
@@ -305,7 +477,11 @@ int fwd512_max_keys() { return G5_MAX_KEYS; }
 
 hipError_t launch_fwd512(const FwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.tiles_per_group * p.n_groups * p.num_splits));
-  if (p.kv_idx != nullptr)
+  // long gathered splits and enough workgroups for two per CU (256 CUs):
+  // the single-stage kernel, two per CU; otherwise the double-buffered one
+  if (p.kv_idx != nullptr && p.chunk >= 256 && grid.x >= 512)
+    hipLaunchKernelGGL(fwd512_pair_kernel, grid, dim3(256), 0, stream, p);
+  else if (p.kv_idx != nullptr)
     hipLaunchKernelGGL(fwd512_kernel<true>, grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(fwd512_kernel<false>, grid, dim3(256), 0, stream, p);

@@ -611,6 +611,9 @@ def test_hd512_flash_topk_benchmarked_size_all_rows(F):
     (200, 100, 512, 2048, "bf16", False),  # two row tiles per token, the second of 36 rows
     (400, 64, 100, 1000, "f32", True),     # four tiles, the last partly past s_k; bad entries
     (300, 64, 1024, 8192, "bf16", False),  # 32 tiles per token
+    (600, 64, 600, 4096, "f32", True),     # two workgroups per CU (long splits, 600 of them):
+                                           # bad entries; its first tokens bit-equal to the
+                                           # double-buffered kernel's small launch
 ])
 def test_hd512_gather_many_tokens(F, T, n_h, s_k, pool, out_dtype, plant):
     """The head-dim-512 gather over more tokens than the chip runs at once:
