@@ -267,7 +267,8 @@ __device__ __forceinline__ void fwd512_body(const FwdParams& p, const bool gathe
 
 // Long gathered splits, two workgroups per CU: one K and one V stage (72 KiB of
 // LDS), the S exchange in the K stage once every wave is past QK^T, K(t+1)
-// issued after the exchange and V(t+1) after PV(t).  A workgroup waits for
+// issued after the exchange and V(t+1) after PV(t); a tile waits for its K
+// before QK^T and for its V only after the exchange.  A workgroup waits for
 // each tile; the other workgroup on its CU computes meanwhile.
 __device__ __forceinline__ void fwd512_pair_body(const FwdParams& p, const WgCoords wc,
                                                  const int plane) {
@@ -385,8 +386,8 @@ __device__ __forceinline__ void fwd512_pair_body(const FwdParams& p, const WgCoo
     issue(rv, 0, sV, VS);
   }
   for (int t = 0; t < n_tiles; ++t) {
-    wait_vmcnt<0>();
-    barrier();  // K(t) and V(t) have landed
+    wait_vmcnt<RPW>();
+    barrier();  // K(t) has landed; V(t), issued after it, may still be in flight
     f32x16 s[1][1];
     w.template qk<1>(s, [&](int, int ds) __attribute__((always_inline)) {
       return *reinterpret_cast<const bf16x8*>(sK + k_lane + ds * 32);
@@ -402,7 +403,8 @@ __device__ __forceinline__ void fwd512_pair_body(const FwdParams& p, const WgCoo
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[0][0][4 * i + e] += o[e];
     }
-    barrier();  // every partial is read: K(t+1) may land
+    wait_vmcnt<0>();
+    barrier();  // V(t) has landed, and every partial is read: K(t+1) may land
     issue(rk, t + 1, sK, KS);
     if ((tile_masked >> t) & 1) {
       const int kbase = t * KT;
