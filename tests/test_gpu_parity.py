@@ -145,6 +145,22 @@ def test_partials_entry_point_planes_are_the_splits(F, hd, pool, s_k, splits):
     _check(out.view(w.B, w.T, w.n_h, hd), lse.view(w.B, w.T, w.n_h), q, k, v, idx, w.scale)
 
 
+def test_partials_through_the_two_workgroup_hd512_gather(F):
+    """fmha_mqa_fwd_partials with gathered splits of 300 keys over 600
+    workgroups (the single-stage kernel, two per CU): each plane is attention
+    over its split's keys."""
+    w = W.make_custom(B=1, T=300, n_h=16, hd=512, s_k=600, pool=4096, out_dtype="f32",
+                      num_splits=2, seed=92)
+    q, k, v, idx = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    o_parts, l_parts = F.fwd_partials(q.to(dev), k.to(dev), v.to(dev), idx.to(dev),
+                                      scale=w.scale, num_splits=2)
+    torch.cuda.synchronize()
+    for i in range(2):
+        _check(o_parts[i], l_parts[i], q, k, v, idx[:, :, 300 * i:300 * (i + 1)].contiguous(),
+               w.scale)
+
+
 @pytest.mark.parametrize("hd", [64, 128, 256])
 @pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
 def test_split_workspace_contents_do_not_matter(F, hd, fill):

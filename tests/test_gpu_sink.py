@@ -66,6 +66,19 @@ def test_fwd_sink_matches_oracle(F, hd, s_k, splits, out_dtype, gather):
     _check(out, lse, q, k, v, idx, w.scale, sink.double().numpy())
 
 
+def test_sink_through_the_two_workgroup_hd512_gather(F):
+    """Long gathered splits at hd 512 over enough tokens for two workgroups
+    per CU run the single-stage kernel; the sink joins in its epilogue."""
+    w = W.make_custom(B=1, T=600, n_h=8, hd=512, s_k=512, out_dtype="f32", pool=4096, seed=91)
+    q, k, v, idx = W.make_inputs(w)
+    sink = _sinks(8, w.s_k)
+    qd, kd, vd, idd, sd = _dev(q, k, v, idx, sink)
+    out, lse = F.fwd(qd, kd, vd, idd, scale=w.scale, out_dtype=torch.float32, num_splits=1,
+                     sink=sd)
+    torch.cuda.synchronize()
+    _check(out, lse, q, k, v, idx, w.scale, sink.double().numpy())
+
+
 @pytest.mark.parametrize("splits", [1, 4])
 def test_minus_inf_sinks_change_nothing(F, splits):
     w = W.make_custom(B=1, T=4, n_h=16, hd=128, s_k=384, out_dtype="bf16", num_splits=splits,
