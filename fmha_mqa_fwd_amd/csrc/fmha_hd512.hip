@@ -31,6 +31,10 @@
 //     QK^T(t) (the barrier of the S exchange), V(t+1) at the start of tile t;
 //     each tile ends with a wait that leaves K(t+2) in flight.  The DMA is
 //     issued from inline assembly, so the compiler adds no waits of its own.
+//   * Gathered splits of 256 keys or more in launches of at least 512
+//     workgroups run fwd512_pair_kernel instead: one K and one V stage, so two
+//     workgroups share a CU and each computes while the other waits for its
+//     rows (the same arithmetic in the same order, so the same results).
 #include "fmha_device.h"
 
 namespace fmha {
